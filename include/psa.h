@@ -1,0 +1,153 @@
+/*
+ * psa.h - C ABI of libpsa.so, the MI355X (gfx950) PSA-block attention path.
+ *
+ * The path (vision-rs book, "Custom Kernels", section "Position-Sensitive
+ * Attention (PSA)"): a QKV convolution's NCHW output [B, qkv_h, H, W], whose
+ * channels are grouped per head as [Q | K | V_lo | V_hi] (each KEY_DIM wide),
+ * is repacked to [4, BH, N, KEY_DIM]; Flash Attention 2 runs once per V half
+ * with HEAD_DIM = KEY_DIM, sharing Q and K; the two outputs are merged back to
+ * NCHW [B, c, H, W]; the V section is also written back out in NCHW for the
+ * residual path. psa_attention_fwd does all of it in one kernel.
+ *
+ * Notation: h = heads, KD = key_dim, N = H*W, BH = B*h, n = y*W + x,
+ * bh = b*h + i (head i of batch item b), qkv_h = 4*h*KD, c = 2*h*KD.
+ * Channel of slot s (0 Q, 1 K, 2 V_lo, 3 V_hi) of head i: i*4*KD + s*KD + d.
+ * Channel of half j (0 lo, 1 hi) of head i in merged/extracted outputs:
+ * i*2*KD + j*KD + d.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers to contiguous row-major buffers, 16-byte
+ *    aligned. The caller owns every buffer; the library allocates nothing,
+ *    keeps no state except a thread-local error string, and never
+ *    synchronizes.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued asynchronously on it.
+ *  - Outputs are overwritten, never accumulated into. Inputs are read only.
+ *  - Every argument is validated before anything is launched. On any error
+ *    nothing is enqueued, nothing is written, the status says which class of
+ *    error it was and psa_last_error() names the entry point and the argument.
+ *  - Element type: PSA_BF16 (bfloat16 storage, float32 accumulation and
+ *    float32 softmax, results rounded to nearest even) or PSA_F32 (float32
+ *    throughout). Layout entry points move bit patterns and never round.
+ *  - KD / head_dim must be one of 16, 32, 64, 128 (FA2's HEAD_DIM is a
+ *    compile-time power of two: vision-rs book, "Custom Kernels", section
+ *    "Flash Attention 2").
+ *  - Input and output byte ranges must not overlap (PSA_ERR_ALIAS).
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef PSA_H
+#define PSA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PSA_ABI_VERSION 1
+
+typedef enum psa_dtype {
+  PSA_F32 = 0,
+  PSA_BF16 = 1
+} psa_dtype;
+
+typedef enum psa_status {
+  PSA_OK = 0,
+  PSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PSA_ERR_SHAPE = 2,       /* a dimension is <= 0 or a size overflows */
+  PSA_ERR_UNSUPPORTED = 3, /* key_dim/head_dim/dtype/scale outside what is built */
+  PSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  PSA_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
+  PSA_ERR_LAUNCH = 6       /* the HIP runtime rejected a launch */
+} psa_status;
+
+/*
+ * PsaPackQkv (vision-rs book, "Custom Kernels", "Position-Sensitive Attention
+ * (PSA)", PsaPackQkv):
+ *   packed[s][b*h+i][n][d] = qkv[b][i*4*KD + s*KD + d][y][x]
+ * qkv_nchw: [B, 4*h*KD, H, W] input.  packed: [4, B*h, H*W, KD] output.
+ * A pure permutation of elements (bit copy).
+ */
+psa_status psa_pack_qkv(const void* qkv_nchw, void* packed, int B, int heads, int key_dim,
+                        int H, int W, psa_dtype dtype, void* stream);
+
+/*
+ * PsaExtractV (same page and section, PsaExtractV: the V section back out in
+ * NCHW for the residual path):
+ *   v_nchw[b][i*2*KD + j*KD + d][y][x] = packed[2+j][b*h+i][n][d]
+ * packed: [4, B*h, H*W, KD] input (only slots 2 and 3 are read).
+ * v_nchw: [B, 2*h*KD, H, W] output. Bit copy.
+ */
+psa_status psa_extract_v(const void* packed, void* v_nchw, int B, int heads, int key_dim,
+                         int H, int W, psa_dtype dtype, void* stream);
+
+/*
+ * PsaMergeAttn (same page and section, PsaMergeAttn: attention output back
+ * into NCHW [B, c, H, W]):
+ *   out_nchw[b][i*2*KD + j*KD + d][y][x] = o2[j][b*h+i][n][d]
+ * o2: [2, B*h, H*W, KD] input (half 0 = attention over V_lo, 1 = over V_hi).
+ * out_nchw: [B, 2*h*KD, H, W] output. Bit copy.
+ */
+psa_status psa_merge_attn(const void* o2, void* out_nchw, int B, int heads, int key_dim,
+                          int H, int W, psa_dtype dtype, void* stream);
+
+/*
+ * Flash Attention 2 forward (vision-rs book, "Custom Kernels", "Flash
+ * Attention 2": online softmax over [BATCH*N_HEADS, N_CTX, HEAD_DIM] tensors;
+ * the n_q x n_k score matrix is never stored):
+ *   o[bh][n][:] = sum_m softmax_m(scale * q[bh][n] . k[bh][m]) * v[bh][m][:]
+ *   lse[bh][n]  = ln sum_m exp(scale * q[bh][n] . k[bh][m])      (natural log)
+ * q: [BH, n_q, head_dim]; k, v: [BH, n_k, head_dim]; o: [BH, n_q, head_dim];
+ * lse: [BH, n_q] float32, or NULL to skip it. No mask, no dropout, no bias.
+ * scale must be finite and > 0.
+ */
+psa_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int BH, int n_q, int n_k, int head_dim, float scale, psa_dtype dtype,
+                   void* stream);
+
+/*
+ * Flash Attention 2 backward: the dQ kernel and the dK/dV kernel are separate
+ * launches with their own grids (vision-rs book, "Custom Kernels", "Flash
+ * Attention 2"). With P = exp(scale*q k^T - lse), Delta = rowsum(dout * o),
+ * dS = P * (dout v^T - Delta):
+ *   dq = scale * dS k,  dk = scale * dS^T q,  dv = P^T dout.
+ * q, o, dout, dq: [BH, n_q, head_dim]; k, v, dk, dv: [BH, n_k, head_dim];
+ * lse: [BH, n_q] float32 as written by fa2_fwd; workspace: caller-owned
+ * float32 scratch of fa2_bwd_workspace_bytes(BH, n_q) bytes (holds Delta).
+ * scale must be the one given to fa2_fwd.
+ */
+psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, float* workspace,
+                   int BH, int n_q, int n_k, int head_dim, float scale, psa_dtype dtype,
+                   void* stream);
+
+/* Bytes of workspace fa2_bwd needs: BH * n_q floats. 0 if a size is invalid. */
+size_t fa2_bwd_workspace_bytes(int BH, int n_q);
+
+/*
+ * The whole PSA forward in one kernel: PsaPackQkv, FA2 over (Q, K, V_lo) and
+ * (Q, K, V_hi) and PsaMergeAttn (vision-rs book, "Custom Kernels",
+ * "Position-Sensitive Attention (PSA)"), fused as teenygrad's book says custom
+ * ops must be ("Your Kernel as a Graph Op", "Where fusion happens"). One
+ * softmax serves both halves, since they share Q and K:
+ *   out_nchw[b][i*2*KD + j*KD + d][y][x] = FA2(Q, K, V_j)[b*h+i][n][d]
+ * qkv_nchw: [B, 4*h*KD, H, W]; out_nchw: [B, 2*h*KD, H, W].
+ * v_nchw: [B, 2*h*KD, H, W] V residual exactly as psa_extract_v writes it, or
+ * NULL to skip it. lse: [B*h, H*W] float32, or NULL.
+ * scale must be finite and > 0 (the PSA block uses key_dim ** -0.5).
+ */
+psa_status psa_attention_fwd(const void* qkv_nchw, void* out_nchw, void* v_nchw, float* lse,
+                             int B, int heads, int key_dim, int H, int W, float scale,
+                             psa_dtype dtype, void* stream);
+
+/* Message of the last error on this thread ("" after a success). */
+const char* psa_last_error(void);
+
+/* PSA_ABI_VERSION of the loaded library. */
+int psa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSA_H */

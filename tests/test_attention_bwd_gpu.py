@@ -1,0 +1,89 @@
+"""FA2 backward (Delta, dK/dV, dQ kernels) on the GPU against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import psa_inputs as I
+import vision_transformer_attention_psapackqkv_amd as psa
+from oracle import psa_oracle as O
+from tests.gpu_helpers import announce, assert_attention_close, device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+# (BH, n_q, n_k, head_dim, dtype): several tiles, ragged tails, every head_dim.
+SHAPES = [
+    (1, 1, 1, 32, "bf16"),
+    (2, 64, 64, 16, "bf16"),
+    (3, 100, 77, 32, "bf16"),
+    (2, 129, 200, 64, "bf16"),
+    (2, 65, 63, 128, "bf16"),
+    (4, 300, 260, 32, "bf16"),
+    (2, 64, 64, 16, "f32"),
+    (3, 100, 77, 32, "f32"),
+    (2, 33, 130, 64, "f32"),
+    (1, 20, 45, 128, "f32"),
+]
+
+
+def _id(s):
+    return "BH{}_q{}_k{}_d{}_{}".format(*s)
+
+
+def _run_bwd(q, k, v, do, dev, o=None, lse=None):
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    if o is None:
+        o, lse = psa.fa2_fwd(qd, kd, vd)
+    return psa.fa2_bwd(qd, kd, vd, o.to(dev), dod, lse.to(dev))
+
+
+def _check(grads, q, k, v, do, dt, sel=None):
+    qq, kk, vv, gg = (to_f64(t) for t in (q, k, v, do))
+    if sel is not None:
+        qq, kk, vv, gg = qq[sel], kk[sel], vv[sel], gg[sel]
+    want = O.attention_bwd(qq, kk, vv, gg, qq.shape[2] ** -0.5)
+    for name, got, w in zip(("dQ", "dK", "dV"), grads, want):
+        g = to_f64(got)
+        if sel is not None:
+            g = g[sel]
+        assert_attention_close(g, w, dt, f"fa2_bwd {name}")
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_id)
+def test_fa2_bwd(shape):
+    dev = device()
+    BH, nq, nk, D, dt = shape
+    announce(f"fa2_bwd {_id(shape)}")
+    q, k, v, do = I.make_attention_inputs(BH, nq, nk, D, dtype=dt, seed=7 * BH + nq + nk + D, with_dout=True)
+    grads = _run_bwd(q, k, v, do, dev)
+    _check(grads, q, k, v, do, dt)
+
+
+@pytest.mark.parametrize("shape", SHAPES[:6], ids=_id)
+def test_fa2_bwd_from_oracle_forward(shape):
+    """O and LSE come from the oracle (O rounded to the storage dtype), isolating the backward."""
+    dev = device()
+    BH, nq, nk, D, dt = shape
+    announce(f"fa2_bwd oracle-fwd {_id(shape)}")
+    q, k, v, do = I.make_attention_inputs(BH, nq, nk, D, dtype=dt, seed=3 * BH + nq + nk + D, with_dout=True)
+    o64, lse64 = O.attention(to_f64(q), to_f64(k), to_f64(v), D ** -0.5)
+    o = torch.from_numpy(o64).to(q.dtype)
+    lse = torch.from_numpy(lse64).to(torch.float32)
+    grads = _run_bwd(q, k, v, do, dev, o=o, lse=lse)
+    _check(grads, q, k, v, do, dt)
+
+
+def test_fa2_bwd_workload_40x40():
+    """The backward workload at full size (BH=256, N=1600, head_dim 32), sampled heads
+    against the oracle, plus an invariant on every head: sum_m dV[m] = sum_n dO[n]."""
+    dev = device()
+    w = I.WORKLOADS["fa2_bwd_bf16_40x40"]
+    announce("fa2_bwd workload 40x40")
+    q, k, v, do = I.make_workload_bwd(w)
+    grads = _run_bwd(q, k, v, do, dev)
+    sel = np.array([0, 1, 127, 255])
+    _check(grads, q, k, v, do, "bf16", sel=sel)
+    dv_sum = to_f64(grads[2]).sum(axis=1)
+    do_sum = to_f64(do).sum(axis=1)
+    # |sum_n dO| is ~40 here; bf16 rounding of P and of each dV element (<= 2^-9 relative)
+    # keeps the difference near 1e-2
+    assert np.abs(dv_sum - do_sum).max() < 0.1, np.abs(dv_sum - do_sum).max()

@@ -1,0 +1,146 @@
+"""FA2 forward and the fused PSA forward on the GPU against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import psa_inputs as I
+import vision_transformer_attention_psapackqkv_amd as psa
+from oracle import psa_oracle as O
+from tests.gpu_helpers import (announce, assert_attention_close, assert_lse_close, bits, device,
+                               to_f64)
+
+pytestmark = pytest.mark.gpu
+
+# (BH, n_q, n_k, head_dim, dtype): several query/key tiles with ragged tails.
+FA2_SHAPES = [
+    (1, 1, 1, 32, "bf16"),
+    (2, 64, 64, 16, "bf16"),
+    (3, 100, 77, 32, "bf16"),
+    (2, 129, 200, 64, "bf16"),
+    (2, 65, 63, 128, "bf16"),
+    (32, 400, 400, 32, "bf16"),
+    (1, 300, 1, 64, "bf16"),
+    (2, 64, 64, 16, "f32"),
+    (3, 100, 77, 32, "f32"),
+    (2, 33, 130, 64, "f32"),
+    (1, 20, 45, 128, "f32"),
+]
+
+
+def _fa2_id(s):
+    return "BH{}_q{}_k{}_d{}_{}".format(*s)
+
+
+@pytest.mark.parametrize("shape", FA2_SHAPES, ids=_fa2_id)
+def test_fa2_fwd(shape):
+    dev = device()
+    BH, nq, nk, D, dt = shape
+    announce(f"fa2_fwd {_fa2_id(shape)}")
+    q, k, v = I.make_attention_inputs(BH, nq, nk, D, dtype=dt, seed=BH + nq + nk + D)
+    s = D ** -0.5
+    o, lse = psa.fa2_fwd(q.to(dev), k.to(dev), v.to(dev), scale=s)
+    want_o, want_lse = O.attention(to_f64(q), to_f64(k), to_f64(v), s)
+    assert_attention_close(to_f64(o), want_o, dt, "fa2_fwd O")
+    assert_lse_close(to_f64(lse), want_lse, dt, "fa2_fwd")
+
+
+# (B, heads, key_dim, H, W, dtype)
+PSA_SHAPES = [
+    (1, 1, 16, 8, 8, "f32"),            # the tiny float32 map
+    (8, 4, 32, 20, 20, "bf16"),         # the 20x20 map, whole
+    (1, 2, 16, 1, 1, "bf16"),           # one pixel: O = V
+    (2, 1, 32, 7, 9, "bf16"),           # N = 63, not a multiple of 8
+    (1, 2, 64, 5, 13, "bf16"),          # N = 65
+    (1, 1, 128, 9, 12, "bf16"),         # key_dim 128, N = 108
+    (2, 2, 64, 16, 16, "bf16"),         # N = 256, whole tiles
+    (1, 2, 32, 3, 3, "f32"),
+    (1, 1, 64, 10, 13, "f32"),
+    (1, 1, 128, 4, 6, "f32"),
+]
+
+
+def _psa_id(s):
+    return "B{}h{}kd{}_{}x{}_{}".format(*s)
+
+
+def _check_psa(qkv, B, h, KD, H, W, dt, out, vres, lse, bh_sel=None):
+    x = to_f64(qkv)
+    if bh_sel is None:
+        want_out, want_v, want_lse = O.psa_forward(x, B, h, KD, H, W)
+        got_out = to_f64(out)
+        got_lse = to_f64(lse)
+    else:
+        # sampled batch-heads: the oracle's attention on those heads' packed slices
+        packed = O.pack_qkv(x, B, h, KD, H, W)
+        s = O.default_scale(KD)
+        o_lo, want_lse = O.attention(packed[0][bh_sel], packed[1][bh_sel], packed[2][bh_sel], s)
+        o_hi, _ = O.attention(packed[0][bh_sel], packed[1][bh_sel], packed[3][bh_sel], s)
+        want_out = np.concatenate([o_lo, o_hi], axis=2)             # [S, N, 2KD]
+        got = to_f64(out).reshape(B * h, 2 * KD, H * W)[bh_sel]      # [S, 2KD, N]
+        got_out = got.transpose(0, 2, 1)
+        got_lse = to_f64(lse)[bh_sel]
+        want_v = None
+    assert_attention_close(got_out, want_out, dt, "psa_attention_fwd out")
+    assert_lse_close(got_lse, want_lse, dt, "psa_attention_fwd")
+    # the V residual is a bit copy of the V channels
+    want_v_bits = O.extract_v(O.pack_qkv(bits(qkv), B, h, KD, H, W), B, h, KD, H, W)
+    assert np.array_equal(bits(vres), want_v_bits), "V residual differs"
+    return want_v
+
+
+@pytest.mark.parametrize("shape", PSA_SHAPES, ids=_psa_id)
+def test_psa_fused_fwd(shape):
+    dev = device()
+    B, h, KD, H, W, dt = shape
+    announce(f"psa_attention_fwd {_psa_id(shape)}")
+    qkv = I.make_qkv(B, h, KD, H, W, dtype=dt, dist="uniform" if dt == "f32" else "normal",
+                     seed=11 * B + h + KD + H * W)
+    out, vres, lse = psa.psa_attention_fwd(qkv.to(dev), h, KD)
+    _check_psa(qkv, B, h, KD, H, W, dt, out, vres, lse)
+
+
+@pytest.mark.parametrize("shape", PSA_SHAPES, ids=_psa_id)
+def test_psa_unfused_fwd(shape):
+    """pack -> fa2_fwd(V_lo) -> fa2_fwd(V_hi) -> merge, plus extract, as separate launches."""
+    dev = device()
+    B, h, KD, H, W, dt = shape
+    announce(f"psa unfused {_psa_id(shape)}")
+    qkv = I.make_qkv(B, h, KD, H, W, dtype=dt, dist="uniform" if dt == "f32" else "normal",
+                     seed=11 * B + h + KD + H * W)
+    packed = psa.psa_pack_qkv(qkv.to(dev), h, KD)
+    o2 = torch.empty((2,) + tuple(packed.shape[1:]), dtype=packed.dtype, device=dev)
+    _, lse = psa.fa2_fwd(packed[0], packed[1], packed[2], out=o2[0])
+    psa.fa2_fwd(packed[0], packed[1], packed[3], out=o2[1], want_lse=False)
+    out = psa.psa_merge_attn(o2, B, h, KD, H, W)
+    vres = psa.psa_extract_v(packed, B, h, KD, H, W)
+    _check_psa(qkv, B, h, KD, H, W, dt, out, vres, lse)
+
+
+@pytest.mark.parametrize("name", ["psa_fwd_bf16_20x20", "psa_fwd_bf16_40x40_peaked", "psa_fwd_bf16_80x80"])
+def test_psa_fused_workloads(name):
+    """The workload maps at full size through the fused entry point (the benchmarked launch),
+    checked on sampled batch-heads (every query row of each sampled head)."""
+    dev = device()
+    w = I.WORKLOADS[name]
+    announce(f"psa_attention_fwd workload {name}")
+    qkv = I.make_workload_qkv(w)
+    out, vres, lse = psa.psa_attention_fwd(qkv.to(dev), w.heads, w.key_dim)
+    sel = np.unique(np.array([0, 1, w.BH // 2, w.BH - 1]))
+    _check_psa(qkv, w.B, w.heads, w.key_dim, w.H, w.W, w.dtype, out, vres, lse, bh_sel=sel)
+
+
+def test_psa_fused_repeatable_and_matches_halves():
+    """Two runs give identical bits; the first half equals an FA2 run on (Q, K, V_lo)
+    to within bf16 tolerance (the fused softmax is shared by both halves)."""
+    dev = device()
+    B, h, KD, H, W = 2, 2, 32, 12, 12
+    announce("psa fused repeatability")
+    qkv = I.make_qkv(B, h, KD, H, W, seed=77).to(dev)
+    o1, _, l1 = psa.psa_attention_fwd(qkv, h, KD)
+    o2, _, l2 = psa.psa_attention_fwd(qkv, h, KD)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    packed = psa.psa_pack_qkv(qkv, h, KD)
+    lo, lse_lo = psa.fa2_fwd(packed[0], packed[1], packed[2])
+    lo_nchw = to_f64(o1).reshape(B * h, 2 * KD, H * W)[:, :KD].transpose(0, 2, 1)
+    assert_attention_close(lo_nchw, to_f64(lo), "bf16", "fused lo half vs fa2_fwd")
+    assert np.abs(to_f64(lse_lo) - to_f64(l1)).max() < 5e-3

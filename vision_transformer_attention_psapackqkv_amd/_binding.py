@@ -1,0 +1,190 @@
+"""ctypes binding of libpsa.so (the C ABI declared in include/psa.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. torch supplies device memory (``torch.empty`` for outputs) and the
+current stream. There is no fallback of any kind: if the library is missing or
+a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpsa.so")
+
+PSA_F32, PSA_BF16 = 0, 1
+STATUS_NAMES = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPPORTED",
+                4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_LAUNCH"}
+
+# Every exported symbol with its ctypes signature (same order and types as include/psa.h).
+_P, _I, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+SIGNATURES = {
+    "psa_pack_qkv": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "psa_extract_v": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "psa_merge_attn": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "fa2_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "fa2_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "fa2_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+    "psa_attention_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "psa_last_error": (ctypes.c_char_p, []),
+    "psa_abi_version": (_I, []),
+}
+
+
+class PsaError(RuntimeError):
+    """A libpsa entry point returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads libpsa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libpsa.so not found at {LIB_PATH}: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PsaError(status, load_library().psa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PSA_BF16
+    if t.dtype == torch.float32:
+        return PSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def default_scale(key_dim: int) -> float:
+    return float(key_dim) ** -0.5
+
+
+def psa_pack_qkv(qkv: torch.Tensor, heads: int, key_dim: int, out: torch.Tensor | None = None):
+    """qkv NCHW ``[B, 4*heads*key_dim, H, W]`` -> packed ``[4, B*heads, H*W, key_dim]``."""
+    _dev(qkv, "qkv")
+    B, C, H, W = qkv.shape
+    if C != 4 * heads * key_dim:
+        raise ValueError(f"qkv has {C} channels, expected 4*heads*key_dim = {4 * heads * key_dim}")
+    if out is None:
+        out = torch.empty((4, B * heads, H * W, key_dim), dtype=qkv.dtype, device=qkv.device)
+    _check(load_library().psa_pack_qkv(qkv.data_ptr(), _dev(out, "out").data_ptr(), B, heads,
+                                       key_dim, H, W, _dtype_code(qkv), _stream(qkv)))
+    return out
+
+
+def _rows_to_nchw(fn_name, rows, slots, B, heads, key_dim, H, W, out):
+    _dev(rows, "input")
+    if tuple(rows.shape) != (slots, B * heads, H * W, key_dim):
+        raise ValueError(f"input shape {tuple(rows.shape)} != {(slots, B * heads, H * W, key_dim)}")
+    if out is None:
+        out = torch.empty((B, 2 * heads * key_dim, H, W), dtype=rows.dtype, device=rows.device)
+    fn = getattr(load_library(), fn_name)
+    _check(fn(rows.data_ptr(), _dev(out, "out").data_ptr(), B, heads, key_dim, H, W,
+              _dtype_code(rows), _stream(rows)))
+    return out
+
+
+def psa_extract_v(packed, B, heads, key_dim, H, W, out=None):
+    """packed ``[4, B*heads, H*W, key_dim]`` -> V residual NCHW ``[B, 2*heads*key_dim, H, W]``."""
+    return _rows_to_nchw("psa_extract_v", packed, 4, B, heads, key_dim, H, W, out)
+
+
+def psa_merge_attn(o2, B, heads, key_dim, H, W, out=None):
+    """o2 ``[2, B*heads, H*W, key_dim]`` -> NCHW ``[B, 2*heads*key_dim, H, W]``."""
+    return _rows_to_nchw("psa_merge_attn", o2, 2, B, heads, key_dim, H, W, out)
+
+
+def fa2_fwd(q, k, v, scale=None, out=None, lse=None, want_lse=True):
+    """FA2 forward on ``[BH, n, D]`` tensors; returns ``(o, lse)`` (lse is None if not wanted)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    BH, n_q, D = q.shape
+    n_k = k.shape[1]
+    if tuple(k.shape) != (BH, n_k, D) or tuple(v.shape) != (BH, n_k, D):
+        raise ValueError("k and v must be [BH, n_k, D] with q's BH and D")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((BH, n_q), dtype=torch.float32, device=q.device)
+    s = default_scale(D) if scale is None else float(scale)
+    _check(load_library().fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dev(out, "out").data_ptr(),
+                                  _ptr(lse), BH, n_q, n_k, D, s, _dtype_code(q), _stream(q)))
+    return out, lse
+
+
+def fa2_bwd(q, k, v, o, dout, lse, scale=None, workspace=None):
+    """FA2 backward; returns ``(dq, dk, dv)``."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse")):
+        _dev(t, n)
+    BH, n_q, D = q.shape
+    n_k = k.shape[1]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    lib = load_library()
+    if workspace is None:
+        nbytes = lib.fa2_bwd_workspace_bytes(BH, n_q)
+        workspace = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=q.device)
+    s = default_scale(D) if scale is None else float(scale)
+    _check(lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       workspace.data_ptr(), BH, n_q, n_k, D, s, _dtype_code(q), _stream(q)))
+    return dq, dk, dv
+
+
+def psa_attention_fwd(qkv, heads, key_dim, scale=None, want_v=True, want_lse=True,
+                      out=None, v_out=None, lse=None):
+    """Fused PSA forward on NCHW ``qkv``; returns ``(out, v_residual, lse)`` (None where not wanted)."""
+    _dev(qkv, "qkv")
+    B, C, H, W = qkv.shape
+    if C != 4 * heads * key_dim:
+        raise ValueError(f"qkv has {C} channels, expected 4*heads*key_dim = {4 * heads * key_dim}")
+    shape = (B, 2 * heads * key_dim, H, W)
+    if out is None:
+        out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device)
+    if v_out is None and want_v:
+        v_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B * heads, H * W), dtype=torch.float32, device=qkv.device)
+    s = default_scale(key_dim) if scale is None else float(scale)
+    _check(load_library().psa_attention_fwd(qkv.data_ptr(), _dev(out, "out").data_ptr(), _ptr(v_out),
+                                            _ptr(lse), B, heads, key_dim, H, W, s,
+                                            _dtype_code(qkv), _stream(qkv)))
+    return out, v_out, lse
+
+
+def psa_abi_version() -> int:
+    return load_library().psa_abi_version()

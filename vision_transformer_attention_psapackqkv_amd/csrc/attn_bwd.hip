@@ -1,0 +1,609 @@
+// Flash Attention 2 backward for gfx950.
+//
+// vision-rs book, "Custom Kernels", section "Flash Attention 2": the dQ
+// backward and the dK/dV backward are separate kernels, each with its own
+// grid. With P = exp(scale*Q K^T - LSE) recomputed from the forward's LSE,
+// Delta = rowsum(dO * O) and dS = P * (dO V^T - Delta):
+//   dV = P^T dO,   dK = scale * dS^T Q,   dQ = scale * dS K.
+// Three launches: Delta (one pass over O and dO), dK/dV (one workgroup per
+// key tile, looping over query tiles) and dQ (one workgroup per query tile,
+// looping over key tiles). Neither uses atomics.
+//
+// The matrix-core products use v_mfma_f32_32x32x16_bf16 with the operand
+// placement of the forward kernel: a product is arranged so that the
+// accumulator of the first product (the scores) is already the register
+// operand of the next one, and the operand read from LDS with the reduction
+// index contiguous is staged transposed (8x8 register transposes on the way
+// in, rows permuted inside each group of 16 like the forward's V^T).
+#include <math.h>
+
+#include "psa_device.hpp"
+#include "psa_launch.hpp"
+
+namespace psa {
+namespace {
+
+constexpr int kPad = 8;
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;     // natural log, [BH, n_q]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;         // [BH, n_q]
+  int BH, n_q, n_k;
+  int tiles;            // workgroups per batch-head
+  float scale;
+  float c;              // scale * log2(e)
+};
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = in[2 * w][c >> 1];
+      const uint32_t hi = in[2 * w + 1][c >> 1];
+      out[c][w] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+  }
+}
+
+// 8 consecutive rows (8*mb .. 8*mb+7 of a tile) of one transposed row, at the
+// permuted positions the MFMA B-operand order needs: inside each group of 16,
+// index kappa goes to 8*((kappa/4)%2) + 4*(kappa/8) + kappa%4.
+__device__ __forceinline__ void store_t8(uint16_t* row, int mb, u32x4 v) {
+  const int base = (mb >> 1) * 16 + (mb & 1) * 4;
+  *reinterpret_cast<u32x2*>(row + base) = u32x2{v[0], v[1]};
+  *reinterpret_cast<u32x2*>(row + base + 8) = u32x2{v[2], v[3]};
+}
+
+__device__ __forceinline__ void block_of(int total, int tiles, int& bh, int& t) {
+  const int i = blockIdx.x;
+  const int per = total / 8;
+  const int L = (i < per * 8) ? (i % 8) * per + i / 8 : i;   // XCD-contiguous runs
+  bh = L / tiles;
+  t = L - bh * tiles;
+}
+
+// ---------------------------------------------------------------- Delta
+
+template <int D, bool kBf16>
+__global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (row >= static_cast<int64_t>(a.BH) * a.n_q) return;
+  float acc = 0.0f;
+  if constexpr (kBf16) {
+    const uint16_t* o = a.o + row * D;
+    const uint16_t* g = a.dout + row * D;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const u32x4 ov = load16(o + c * 8), gv = load16(g + c * 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(__builtin_bit_cast(float, ov[w] << 16), __builtin_bit_cast(float, gv[w] << 16), acc);
+        acc = fmaf(__builtin_bit_cast(float, ov[w] & 0xFFFF0000u),
+                   __builtin_bit_cast(float, gv[w] & 0xFFFF0000u), acc);
+      }
+    }
+  } else {
+    const float* o = reinterpret_cast<const float*>(a.o) + row * D;
+    const float* g = reinterpret_cast<const float*>(a.dout) + row * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc = fmaf(o[d], g[d], acc);
+  }
+  a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------- dK / dV (bf16)
+
+template <int D, int kWaves>
+struct DkdvTile {
+  static constexpr int NT = kWaves * 64;
+  static constexpr int BQ = 64;                    // queries per tile
+  static constexpr int DP = D < 32 ? 32 : D;       // transposed rows, padded to one MFMA block
+  static constexpr int RSTR = D + kPad;            // [q][d] tiles
+  static constexpr int TSTR = BQ + kPad;           // [d][q] tiles
+  static constexpr int R_ELEMS = BQ * RSTR;
+  static constexpr int T_ELEMS = DP * TSTR;
+  // Layout of one buffer (bf16 elements, then floats).
+  static constexpr int OFF_Q = 0, OFF_DO = R_ELEMS, OFF_QT = 2 * R_ELEMS, OFF_DOT = 2 * R_ELEMS + T_ELEMS;
+  static constexpr int H_ELEMS = 2 * R_ELEMS + 2 * T_ELEMS;   // bf16 elements (even count)
+  static constexpr int BUF_BYTES = H_ELEMS * 2 + 2 * BQ * 4;
+  static constexpr int BLOCKS = 2 * (BQ / 8) * (D / 8);      // 8x8 blocks of Q and dO
+  static_assert(BLOCKS <= NT, "one 8x8 block per thread");
+
+  u32x4 r[8];
+  float l2, dl;
+
+  __device__ __forceinline__ void load(const BwdArgs& a, int bh, int qt, int tid) {
+    const int q0 = qt * BQ;
+    if (tid < BLOCKS) {
+      const int which = tid / (BLOCKS / 2);          // 0: Q, 1: dO
+      const int b = tid % (BLOCKS / 2);
+      const int mb = b / (D / 8), db = b % (D / 8);
+      const uint16_t* src = which ? a.dout : a.q;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int qq = q0 + mb * 8 + i;
+        r[i] = (qq < a.n_q) ? load16(src + (static_cast<int64_t>(bh) * a.n_q + qq) * D + db * 8) : zero4();
+      }
+    }
+    if (tid < BQ) {
+      const int qq = q0 + tid;
+      const bool ok = qq < a.n_q;
+      // Rows past n_q get P = 0 (LSE = +inf) and Delta = 0.
+      l2 = ok ? a.lse[static_cast<int64_t>(bh) * a.n_q + qq] * kLog2e : INFINITY;
+      dl = ok ? a.delta[static_cast<int64_t>(bh) * a.n_q + qq] : 0.0f;
+    }
+  }
+
+  __device__ __forceinline__ void store(char* buf, int tid) const {
+    uint16_t* h = reinterpret_cast<uint16_t*>(buf);
+    float* f = reinterpret_cast<float*>(buf + H_ELEMS * 2);
+    if (tid < BLOCKS) {
+      const int which = tid / (BLOCKS / 2);
+      const int b = tid % (BLOCKS / 2);
+      const int mb = b / (D / 8), db = b % (D / 8);
+      uint16_t* rows = h + (which ? OFF_DO : OFF_Q);
+      uint16_t* tr = h + (which ? OFF_DOT : OFF_QT);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(rows + (mb * 8 + i) * RSTR + db * 8) = r[i];
+      u32x4 t[8];
+      transpose8x8(r, t);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) store_t8(tr + (db * 8 + c) * TSTR, mb, t[c]);
+    }
+    if (tid < BQ) {
+      f[tid] = l2;
+      f[BQ + tid] = dl;
+    }
+  }
+};
+
+template <int D, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_bf16(BwdArgs a) {
+  using Tile = DkdvTile<D, kWaves>;
+  constexpr int BQ = Tile::BQ;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = Tile::DP / 32;
+  __shared__ __attribute__((aligned(16))) char smem[2 * Tile::BUF_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  int bh, kt;
+  block_of(a.BH * a.tiles, a.tiles, bh, kt);
+  const int key = kt * 32 * kWaves + wave * 32 + l32;
+  const bool k_ok = key < a.n_k;
+
+  // Padded transposed rows (D = 16) stay zero.
+  if constexpr (Tile::DP > D) {
+    for (int b = 0; b < 2; ++b) {
+      uint16_t* h = reinterpret_cast<uint16_t*>(smem + b * Tile::BUF_BYTES);
+      for (int e = tid; e < (Tile::DP - D) * Tile::TSTR; e += Tile::NT) {
+        h[Tile::OFF_QT + D * Tile::TSTR + e] = 0;
+        h[Tile::OFF_DOT + D * Tile::TSTR + e] = 0;
+      }
+    }
+  }
+
+  // This lane's key and value rows as B operands: K[key][16ds + 8g + j].
+  bf16x8 kop[NDS], vop[NDS];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) {
+    const int64_t off = (static_cast<int64_t>(bh) * a.n_k + key) * D + ds * 16 + g * 8;
+    kop[ds] = as_bf16x8(k_ok ? load16(a.k + off) : zero4());
+    vop[ds] = as_bf16x8(k_ok ? load16(a.v + off) : zero4());
+  }
+  f32x16 dk_acc[NDB], dv_acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk_acc[db][r] = dv_acc[db][r] = 0.0f;
+
+  const int n_tiles = (a.n_q + BQ - 1) / BQ;
+  Tile tile;
+  tile.load(a, bh, 0, tid);
+  tile.store(smem, tid);
+  __syncthreads();
+
+  for (int qt = 0; qt < n_tiles; ++qt) {
+    const char* buf = smem + (qt & 1) * Tile::BUF_BYTES;
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(buf);
+    const float* f = reinterpret_cast<const float*>(buf + Tile::H_ELEMS * 2);
+    const bool more = qt + 1 < n_tiles;
+    if (more) tile.load(a, bh, qt + 1, tid);
+
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries.
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int off = (qb * 32 + l32) * Tile::RSTR + ds * 16 + g * 8;
+        sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_Q + off), kop[ds], sacc);
+        pacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_DO + off), vop[ds], pacc);
+      }
+      // P and dS at the lane's queries qb*32 + 8*(r/4) + 4g + r%4.
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ql = qb * 32 + 8 * r4 + 4 * g;
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(f + ql);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(f + BQ + ql);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const float p = fast_exp2(fmaf(sacc[r], a.c, -l2[e]));
+          const float dsv = p * (pacc[r] - dl[e]);
+          pb[r >> 3][r & 7] = static_cast<__bf16>(p);
+          sb[r >> 3][r & 7] = static_cast<__bf16>(dsv);
+        }
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the 32 queries, 2 steps of 16).
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int off = (db * 32 + l32) * Tile::TSTR + (qb * 2 + s) * 16 + g * 8;
+          dv_acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_DOT + off), pb[s], dv_acc[db]);
+          dk_acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_QT + off), sb[s], dk_acc[db]);
+        }
+    }
+    if (more) tile.store(smem + ((qt + 1) & 1) * Tile::BUF_BYTES, tid);
+    __syncthreads();
+  }
+
+  if (!k_ok) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + 8 * r4 + 4 * g;
+      if (d0 >= D) continue;
+      const int64_t off = (static_cast<int64_t>(bh) * a.n_k + key) * D + d0;
+      uint32_t kw[2], vw[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        kw[e] = float_to_bf16_bits(dk_acc[db][4 * r4 + 2 * e] * a.scale) |
+                (uint32_t(float_to_bf16_bits(dk_acc[db][4 * r4 + 2 * e + 1] * a.scale)) << 16);
+        vw[e] = float_to_bf16_bits(dv_acc[db][4 * r4 + 2 * e]) |
+                (uint32_t(float_to_bf16_bits(dv_acc[db][4 * r4 + 2 * e + 1])) << 16);
+      }
+      *reinterpret_cast<u32x2*>(a.dk + off) = u32x2{kw[0], kw[1]};
+      *reinterpret_cast<u32x2*>(a.dv + off) = u32x2{vw[0], vw[1]};
+    }
+}
+
+// ---------------------------------------------------------------- dQ (bf16)
+
+template <int D, int kWaves>
+struct DqTile {
+  static constexpr int NT = kWaves * 64;
+  static constexpr int BN = 64;                    // keys per tile
+  static constexpr int DP = D < 32 ? 32 : D;
+  static constexpr int RSTR = D + kPad;
+  static constexpr int TSTR = BN + kPad;
+  static constexpr int R_ELEMS = BN * RSTR;
+  static constexpr int T_ELEMS = DP * TSTR;
+  static constexpr int OFF_K = 0, OFF_V = R_ELEMS, OFF_KT = 2 * R_ELEMS;
+  static constexpr int BUF = 2 * R_ELEMS + T_ELEMS;
+  static constexpr int KBLOCKS = (BN / 8) * (D / 8);   // 8x8 blocks of K (rows + transposed)
+  static constexpr int VCHUNKS = BN * D / 8;           // 16-byte pieces of V rows
+  static constexpr int V_PER = (VCHUNKS + NT - 1) / NT;
+  static_assert(KBLOCKS <= NT, "one K block per thread");
+
+  u32x4 kr[8];
+  u32x4 vr[V_PER];
+
+  __device__ __forceinline__ void load(const BwdArgs& a, int bh, int kt, int tid) {
+    const int m0 = kt * BN;
+    if (tid < KBLOCKS) {
+      const int mb = tid / (D / 8), db = tid % (D / 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + mb * 8 + i;
+        kr[i] = (m < a.n_k) ? load16(a.k + (static_cast<int64_t>(bh) * a.n_k + m) * D + db * 8) : zero4();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+      const int c = tid + i * NT;
+      if (c < VCHUNKS) {
+        const int r = c / (D / 8), cb = c % (D / 8);
+        const int m = m0 + r;
+        vr[i] = (m < a.n_k) ? load16(a.v + (static_cast<int64_t>(bh) * a.n_k + m) * D + cb * 8) : zero4();
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* buf, int tid) const {
+    if (tid < KBLOCKS) {
+      const int mb = tid / (D / 8), db = tid % (D / 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(buf + OFF_K + (mb * 8 + i) * RSTR + db * 8) = kr[i];
+      u32x4 t[8];
+      transpose8x8(kr, t);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) store_t8(buf + OFF_KT + (db * 8 + c) * TSTR, mb, t[c]);
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+      const int c = tid + i * NT;
+      if (c < VCHUNKS) {
+        const int r = c / (D / 8), cb = c % (D / 8);
+        *reinterpret_cast<u32x4*>(buf + OFF_V + r * RSTR + cb * 8) = vr[i];
+      }
+    }
+  }
+};
+
+template <int D, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void bwd_dq_bf16(BwdArgs a) {
+  using Tile = DqTile<D, kWaves>;
+  constexpr int BN = Tile::BN;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = Tile::DP / 32;
+  constexpr int BM = 32 * kWaves;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Tile::BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  int bh, qt;
+  block_of(a.BH * a.tiles, a.tiles, bh, qt);
+  const int q = qt * BM + wave * 32 + l32;
+  const bool q_ok = q < a.n_q;
+
+  if constexpr (Tile::DP > D) {
+    for (int e = tid; e < (Tile::DP - D) * Tile::TSTR; e += Tile::NT) {
+      smem[Tile::OFF_KT + D * Tile::TSTR + e] = 0;
+      smem[Tile::BUF + Tile::OFF_KT + D * Tile::TSTR + e] = 0;
+    }
+  }
+
+  bf16x8 qop[NDS], gop[NDS];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) {
+    const int64_t off = (static_cast<int64_t>(bh) * a.n_q + q) * D + ds * 16 + g * 8;
+    qop[ds] = as_bf16x8(q_ok ? load16(a.q + off) : zero4());
+    gop[ds] = as_bf16x8(q_ok ? load16(a.dout + off) : zero4());
+  }
+  const float l2 = q_ok ? a.lse[static_cast<int64_t>(bh) * a.n_q + q] * kLog2e : 0.0f;
+  const float dl = q_ok ? a.delta[static_cast<int64_t>(bh) * a.n_q + q] : 0.0f;
+  f32x16 dq_acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.0f;
+
+  const int n_tiles = (a.n_k + BN - 1) / BN;
+  Tile tile;
+  tile.load(a, bh, 0, tid);
+  tile.store(smem, tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const uint16_t* buf = smem + (kt & 1) * Tile::BUF;
+    const bool more = kt + 1 < n_tiles;
+    if (more) tile.load(a, bh, kt + 1, tid);
+
+    bf16x8 sb[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T.
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int off = (kb * 32 + l32) * Tile::RSTR + ds * 16 + g * 8;
+        sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_K + off), qop[ds], sacc);
+        pacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_V + off), gop[ds], pacc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
+        if (key >= a.n_k) p = 0.0f;
+        sb[kb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pacc[r] - dl));
+      }
+    }
+    // dQ^T += K^T dS^T (reduction over the tile's keys).
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int s = 0; s < BN / 16; ++s) {
+        const int off = (db * 32 + l32) * Tile::TSTR + s * 16 + g * 8;
+        dq_acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_KT + off), sb[s], dq_acc[db]);
+      }
+    if (more) tile.store(smem + ((kt + 1) & 1) * Tile::BUF, tid);
+    __syncthreads();
+  }
+
+  if (!q_ok) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + 8 * r4 + 4 * g;
+      if (d0 >= D) continue;
+      uint32_t w[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        w[e] = float_to_bf16_bits(dq_acc[db][4 * r4 + 2 * e] * a.scale) |
+               (uint32_t(float_to_bf16_bits(dq_acc[db][4 * r4 + 2 * e + 1] * a.scale)) << 16);
+      *reinterpret_cast<u32x2*>(a.dq + (static_cast<int64_t>(bh) * a.n_q + q) * D + d0) = u32x2{w[0], w[1]};
+    }
+}
+
+// ---------------------------------------------------------------- float32
+
+constexpr int kF32Threads = 128;
+constexpr int kF32Rows = 32;
+
+// dK/dV: one thread per key, queries staged through LDS.
+template <int D>
+__global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32(BwdArgs a) {
+  __shared__ float qs[kF32Rows][D];
+  __shared__ float gs[kF32Rows][D];
+  __shared__ float ls[kF32Rows], dls[kF32Rows];
+  const float* Q = reinterpret_cast<const float*>(a.q);
+  const float* G = reinterpret_cast<const float*>(a.dout);
+  const int blocks = (a.n_k + kF32Threads - 1) / kF32Threads;
+  const int bh = blockIdx.x / blocks;
+  const int key = (blockIdx.x % blocks) * kF32Threads + threadIdx.x;
+  const bool ok = key < a.n_k;
+  float kr[D], vr[D], dk[D], dv[D];
+  const int64_t krow = (static_cast<int64_t>(bh) * a.n_k + (ok ? key : 0)) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    kr[d] = ok ? reinterpret_cast<const float*>(a.k)[krow + d] : 0.0f;
+    vr[d] = ok ? reinterpret_cast<const float*>(a.v)[krow + d] : 0.0f;
+    dk[d] = dv[d] = 0.0f;
+  }
+  for (int q0 = 0; q0 < a.n_q; q0 += kF32Rows) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kF32Rows * D; e += kF32Threads) {
+      const int r = e / D, d = e % D;
+      const bool in = q0 + r < a.n_q;
+      const int64_t i = (static_cast<int64_t>(bh) * a.n_q + q0 + r) * D + d;
+      qs[r][d] = in ? Q[i] : 0.0f;
+      gs[r][d] = in ? G[i] : 0.0f;
+    }
+    if (threadIdx.x < kF32Rows) {
+      const int r = threadIdx.x;
+      const bool in = q0 + r < a.n_q;
+      ls[r] = in ? a.lse[static_cast<int64_t>(bh) * a.n_q + q0 + r] : 0.0f;
+      dls[r] = in ? a.delta[static_cast<int64_t>(bh) * a.n_q + q0 + r] : 0.0f;
+    }
+    __syncthreads();
+    const int cnt = min(kF32Rows, a.n_q - q0);
+    for (int r = 0; r < cnt; ++r) {
+      float s = 0.0f, dp = 0.0f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(qs[r][d], kr[d], s);
+        dp = fmaf(gs[r][d], vr[d], dp);
+      }
+      const float p = expf(s * a.scale - ls[r]);
+      const float ds = p * (dp - dls[r]);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        dv[d] = fmaf(p, gs[r][d], dv[d]);
+        dk[d] = fmaf(ds, qs[r][d], dk[d]);
+      }
+    }
+  }
+  if (!ok) return;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    reinterpret_cast<float*>(a.dk)[krow + d] = dk[d] * a.scale;
+    reinterpret_cast<float*>(a.dv)[krow + d] = dv[d];
+  }
+}
+
+// dQ: one thread per query, keys staged through LDS.
+template <int D>
+__global__ __launch_bounds__(kF32Threads) void bwd_dq_f32(BwdArgs a) {
+  __shared__ float ks[kF32Rows][D];
+  __shared__ float vs[kF32Rows][D];
+  const float* K = reinterpret_cast<const float*>(a.k);
+  const float* V = reinterpret_cast<const float*>(a.v);
+  const int blocks = (a.n_q + kF32Threads - 1) / kF32Threads;
+  const int bh = blockIdx.x / blocks;
+  const int q = (blockIdx.x % blocks) * kF32Threads + threadIdx.x;
+  const bool ok = q < a.n_q;
+  const int64_t qrow = (static_cast<int64_t>(bh) * a.n_q + (ok ? q : 0)) * D;
+  float qr[D], gr[D], dq[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qr[d] = ok ? reinterpret_cast<const float*>(a.q)[qrow + d] : 0.0f;
+    gr[d] = ok ? reinterpret_cast<const float*>(a.dout)[qrow + d] : 0.0f;
+    dq[d] = 0.0f;
+  }
+  const float lse = ok ? a.lse[static_cast<int64_t>(bh) * a.n_q + q] : 0.0f;
+  const float dl = ok ? a.delta[static_cast<int64_t>(bh) * a.n_q + q] : 0.0f;
+  for (int m0 = 0; m0 < a.n_k; m0 += kF32Rows) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kF32Rows * D; e += kF32Threads) {
+      const int r = e / D, d = e % D;
+      const bool in = m0 + r < a.n_k;
+      const int64_t i = (static_cast<int64_t>(bh) * a.n_k + m0 + r) * D + d;
+      ks[r][d] = in ? K[i] : 0.0f;
+      vs[r][d] = in ? V[i] : 0.0f;
+    }
+    __syncthreads();
+    const int cnt = min(kF32Rows, a.n_k - m0);
+    for (int r = 0; r < cnt; ++r) {
+      float s = 0.0f, dp = 0.0f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(qr[d], ks[r][d], s);
+        dp = fmaf(gr[d], vs[r][d], dp);
+      }
+      const float ds = expf(s * a.scale - lse) * (dp - dl);
+#pragma unroll
+      for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, ks[r][d], dq[d]);
+    }
+  }
+  if (!ok) return;
+#pragma unroll
+  for (int d = 0; d < D; ++d) reinterpret_cast<float*>(a.dq)[qrow + d] = dq[d] * a.scale;
+}
+
+// ---------------------------------------------------------------- dispatch
+
+constexpr int kWavesBwd = 4;
+
+template <int D>
+hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(a.BH) * a.n_q;
+  const dim3 grid_delta(static_cast<unsigned>((rows + 255) / 256));
+  if (bf16) {
+    bwd_delta<D, true><<<grid_delta, 256, 0, stream>>>(a);
+    BwdArgs kv = a;
+    kv.tiles = (a.n_k + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
+    bwd_dkdv_bf16<D, kWavesBwd><<<dim3(static_cast<unsigned>(a.BH) * kv.tiles), kWavesBwd * 64, 0, stream>>>(kv);
+    BwdArgs qa = a;
+    qa.tiles = (a.n_q + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
+    bwd_dq_bf16<D, kWavesBwd><<<dim3(static_cast<unsigned>(a.BH) * qa.tiles), kWavesBwd * 64, 0, stream>>>(qa);
+  } else {
+    bwd_delta<D, false><<<grid_delta, 256, 0, stream>>>(a);
+    const unsigned kb = (a.n_k + kF32Threads - 1) / kF32Threads;
+    bwd_dkdv_f32<D><<<dim3(kb * a.BH), kF32Threads, 0, stream>>>(a);
+    const unsigned qb = (a.n_q + kF32Threads - 1) / kF32Threads;
+    bwd_dq_f32<D><<<dim3(qb * a.BH), kF32Threads, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          float* delta, int BH, int n_q, int n_k, int D, float scale, bool bf16,
+                          hipStream_t stream) {
+  BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+            static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
+            static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
+            static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), delta, BH, n_q, n_k, 0,
+            scale, scale * kLog2e};
+  switch (D) {
+    case 16: return run<16>(a, bf16, stream);
+    case 32: return run<32>(a, bf16, stream);
+    case 64: return run<64>(a, bf16, stream);
+    case 128: return run<128>(a, bf16, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace psa

@@ -1,0 +1,34 @@
+// Host-side launchers of the libpsa kernels. Arguments are validated by the
+// C-ABI layer (psa_abi.cpp) before any of these is called; the launchers only
+// pick a template instance and a grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psa {
+
+// PsaPackQkv: qkv [BH*4, KD, N] (the NCHW tensor viewed per head) -> packed [4, BH, N, KD].
+hipError_t launch_pack_qkv(const void* qkv, void* packed, int BH, int KD, int N, int elt_bytes,
+                           hipStream_t stream);
+
+// PsaMergeAttn (slot0 = 0, rows = o2 [2, BH, N, KD]) and PsaExtractV (slot0 = 2,
+// rows = packed [4, BH, N, KD]): rows[slot0 + j][bh] -> nchw [BH*2, KD, N].
+hipError_t launch_rows_to_nchw(const void* rows, void* nchw, int BH, int KD, int N, int slot0,
+                               int elt_bytes, hipStream_t stream);
+
+// FA2 forward on [BH, n, D] tensors.
+hipError_t launch_fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                          int n_q, int n_k, int D, float scale, bool bf16, hipStream_t stream);
+
+// Fused PSA forward: qkv [B, 4hKD, H, W] -> out [B, 2hKD, H, W] (+ V residual, + LSE).
+hipError_t launch_psa_fused_fwd(const void* qkv, void* out, void* vres, float* lse, int BH, int KD,
+                                int N, float scale, bool bf16, hipStream_t stream);
+
+// FA2 backward: Delta into workspace, then the dK/dV and dQ kernels.
+hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          float* delta, int BH, int n_q, int n_k, int D, float scale, bool bf16,
+                          hipStream_t stream);
+
+}  // namespace psa
