@@ -1,0 +1,254 @@
+"""Benchmark of the PSA attention hot path on one MI355X.
+
+One step = one fused PSA forward (psa_attention_fwd: PsaPackQkv + FA2 over
+V_lo and V_hi + PsaMergeAttn in one kernel, writing the NCHW output, the NCHW
+V residual and the LSE) over the 80x80 workload map (B=4, heads=8,
+KEY_DIM=64, N=6400, bf16, synthetic N(0,1) input). ``value`` is its
+throughput in TFLOP/s, counting the algorithmic 6*BH*N^2*KEY_DIM flops
+(Q K^T once, P [V_lo | V_hi]).
+
+Also measured and reported in the same JSON line: the unfused chain (pack,
+FA2 x2, merge, extract), the layout kernels' GB/s against HBM peak (input and
+output buffers rotated over 4 sets larger than the 256 MB Infinity Cache), the
+40x40 forward and the FA2 backward workload. The CPU oracle is timed on a
+bounded sample of the same workload as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "PSA attention fwd TFLOP/s + % bf16 MFMA peak; pack/merge GB/s % HBM"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
+WORKLOAD = "psa_fwd_bf16_80x80"
+ATTN_KERNEL_SRC = os.path.join(ROOT, "vision_transformer_attention_psapackqkv_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_psa_fused_fwd_80x80.json")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time only the fused step (for profiler runs)")
+    return ap.parse_args()
+
+
+def fwd_flops(BH, N, KD):
+    return 6.0 * BH * N * N * KD
+
+
+def time_events(fn, steps, warmup, torch):
+    """Average and total duration (ms) of `fn` launches, HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn(warmup + i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(per) / len(per), min(per), wall
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(per_launch_flops):
+    """HBM bytes per launch of the fused kernel from committed PMC counters, if still current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_sha(ATTN_KERNEL_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(qkv_cpu, w):
+    """The float64 oracle on a bounded sample of the workload (whole batch-heads)."""
+    import numpy as np
+    from oracle import psa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = qkv_cpu.to(dtype=__import__("torch").float64).numpy()
+    packed = O.pack_qkv(x, w.B, w.heads, w.key_dim, w.H, w.W)
+    s = O.default_scale(w.key_dim)
+    done, t0 = 0, time.perf_counter()
+    while done < w.BH and time.perf_counter() - t0 < 10.0:
+        sl = slice(done, done + 1)
+        O.attention(packed[0][sl], packed[1][sl], packed[2][sl], s)
+        O.attention(packed[0][sl], packed[1][sl], packed[3][sl], s)
+        done += 1
+    el = time.perf_counter() - t0
+    flops = fwd_flops(done, w.N, w.key_dim)
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 oracle attention (both V halves) on {done} of {w.BH} batch-heads "
+                      f"of the {w.name} map, {el:.1f} s wall; pack timed once outside"}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1. (Every batch-head is "
+              "an independent problem, so several GPUs would each run this same kernel on their "
+              "share of the batch with no exchange; that mode is not built here.)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import psa_inputs as I
+    import vision_transformer_attention_psapackqkv_amd as psa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = I.WORKLOADS[WORKLOAD]
+    qkv_cpu = I.make_workload_qkv(w)
+    qkv = qkv_cpu.to(dev)
+    out = torch.empty((w.B, w.out_channels, w.H, w.W), dtype=torch.bfloat16, device=dev)
+    vres = torch.empty_like(out)
+    lse = torch.empty((w.BH, w.N), dtype=torch.float32, device=dev)
+
+    def step(_i):
+        psa.psa_attention_fwd(qkv, w.heads, w.key_dim, out=out, v_out=vres, lse=lse)
+
+    # ---- the timed region: exactly `steps` fused forward steps
+    for _ in range(args.warmup):
+        step(0)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    per_launch = []
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        marks[i][0].record()
+        step(i)
+        marks[i][1].record()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per_launch = [a.elapsed_time(b) for a, b in marks]
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    kernel_ms = sum(per_launch) / len(per_launch)
+    flops = fwd_flops(w.BH, w.N, w.key_dim)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = load_traffic(flops)
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "heads": w.heads, "key_dim": w.key_dim,
+                   "H": w.H, "W": w.W, "N": w.N, "path": "psa_attention_fwd (fused)",
+                   "parallelism": "single GPU"},
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16<64,128,NCHW>",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "avg_kernel_ms": round(kernel_ms, 5), "flops_per_launch": flops},
+        "wall_ms_timed_region": round(wall_ms, 3),
+    }
+
+    if not args.only_step:
+        result["components"] = components(torch, psa, I, w, qkv, args)
+    if not args.no_cpu_baseline and not args.only_step:
+        result["cpu_baseline"] = cpu_baseline(qkv_cpu, w)
+    print(json.dumps(result), flush=True)
+
+
+def components(torch, psa, I, w, qkv, args):
+    """Side measurements: unfused chain, layout GB/s, other workloads."""
+    dev = qkv.device
+    steps, warm = max(args.steps, 10), max(args.warmup, 3)
+    comp = {}
+    B, h, KD, H, W = w.B, w.heads, w.key_dim, w.H, w.W
+    # Layout kernels over 4 rotated buffer sets (4 x 210 MB > 256 MB Infinity Cache).
+    sets = 4
+    qkvs = [qkv] + [qkv.clone() for _ in range(sets - 1)]
+    packs = [torch.empty((4, w.BH, w.N, KD), dtype=qkv.dtype, device=dev) for _ in range(sets)]
+    outs = [torch.empty((B, w.out_channels, H, W), dtype=qkv.dtype, device=dev) for _ in range(sets)]
+    elt = 2
+    e_qkv = B * w.qkv_channels * w.N
+    e_out = B * w.out_channels * w.N
+    layout = {
+        "pack": (lambda i: psa.psa_pack_qkv(qkvs[i % sets], h, KD, out=packs[i % sets]), 2 * e_qkv * elt),
+        "merge": (lambda i: psa.psa_merge_attn(packs[i % sets][:2], B, h, KD, H, W, out=outs[i % sets]), 2 * e_out * elt),
+        "extract": (lambda i: psa.psa_extract_v(packs[i % sets], B, h, KD, H, W, out=outs[i % sets]), 2 * e_out * elt),
+    }
+    for name, (fn, nbytes) in layout.items():
+        avg, best, _ = time_events(fn, steps, warm, torch)
+        gbps = nbytes / (avg * 1e-3) / 1e9
+        comp[name] = {"avg_ms": round(avg, 5), "min_ms": round(best, 5), "bytes": nbytes,
+                      "GB/s": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2)}
+    # Unfused chain on the same map: pack, FA2(V_lo), FA2(V_hi), merge, extract.
+    o2 = torch.empty((2, w.BH, w.N, KD), dtype=qkv.dtype, device=dev)
+    lse = torch.empty((w.BH, w.N), dtype=torch.float32, device=dev)
+    pk, out = packs[0], outs[0]
+
+    def unfused(_i):
+        psa.psa_pack_qkv(qkv, h, KD, out=pk)
+        psa.fa2_fwd(pk[0], pk[1], pk[2], out=o2[0], lse=lse)
+        psa.fa2_fwd(pk[0], pk[1], pk[3], out=o2[1], want_lse=False)
+        psa.psa_merge_attn(o2, B, h, KD, H, W, out=out)
+        psa.psa_extract_v(pk, B, h, KD, H, W, out=outs[1])
+
+    avg, best, _ = time_events(unfused, steps, warm, torch)
+    comp["unfused_chain"] = {"avg_ms": round(avg, 5), "TFLOP/s": round(fwd_flops(w.BH, w.N, KD) / (avg * 1e-3) / 1e12, 3)}
+    fa_avg, _, _ = time_events(lambda i: psa.fa2_fwd(pk[0], pk[1], pk[2], out=o2[0], lse=lse), steps, warm, torch)
+    comp["fa2_fwd_one_half"] = {"avg_ms": round(fa_avg, 5),
+                                "TFLOP/s": round(4.0 * w.BH * w.N ** 2 * KD / (fa_avg * 1e-3) / 1e12, 3)}
+    # The 40x40 forward workload (fused).
+    w2 = I.WORKLOADS["psa_fwd_bf16_40x40_peaked"]
+    q2 = I.make_workload_qkv(w2).to(dev)
+    o_2 = torch.empty((w2.B, w2.out_channels, w2.H, w2.W), dtype=q2.dtype, device=dev)
+    v_2 = torch.empty_like(o_2)
+    l_2 = torch.empty((w2.BH, w2.N), dtype=torch.float32, device=dev)
+    avg, _, _ = time_events(lambda i: psa.psa_attention_fwd(q2, w2.heads, w2.key_dim, out=o_2, v_out=v_2, lse=l_2),
+                            steps, warm, torch)
+    t2 = fwd_flops(w2.BH, w2.N, w2.key_dim) / (avg * 1e-3) / 1e12
+    comp["fused_fwd_40x40"] = {"avg_ms": round(avg, 5), "TFLOP/s": round(t2, 3),
+                               "pct_bf16_mfma_peak": round(100 * t2 / PEAK_BF16_TFLOPS, 2)}
+    del q2, o_2, v_2, l_2
+    # The FA2 backward workload (Delta + dK/dV + dQ launches).
+    wb = I.WORKLOADS["fa2_bwd_bf16_40x40"]
+    q, k, v, do = (t.to(dev) for t in I.make_workload_bwd(wb))
+    o, lse_b = psa.fa2_fwd(q, k, v)
+    ws = torch.empty((wb.BH * wb.N,), dtype=torch.float32, device=dev)
+    avg, _, _ = time_events(lambda i: psa.fa2_bwd(q, k, v, o, do, lse_b, workspace=ws), steps, warm, torch)
+    tb = 10.0 * wb.BH * wb.N ** 2 * wb.key_dim / (avg * 1e-3) / 1e12
+    comp["fa2_bwd_40x40"] = {"avg_ms": round(avg, 5), "TFLOP/s": round(tb, 3),
+                             "pct_bf16_mfma_peak": round(100 * tb / PEAK_BF16_TFLOPS, 2),
+                             "flops": "10*BH*N^2*D"}
+    return comp
+
+
+if __name__ == "__main__":
+    main()
