@@ -9,24 +9,31 @@
 //
 // Work decomposition (ours, not the page's one-program-per-query-row): one
 // workgroup per (batch-head, tile of 32*kWaves queries); each wave owns 32
-// queries and walks all keys in tiles of 64 staged in LDS (double-buffered,
-// the next tile's global loads in flight while the current one is computed).
+// queries and walks all keys in tiles of 64, staged in LDS by plain 16-byte
+// copies in the tensors' own layout (double-buffered: the next tile's global
+// loads are in flight while the current tile is computed).
 //
 // Per wave and key tile, on the matrix cores (v_mfma_f32_32x32x16_bf16):
-//   S^T[key][query] = K Q^T      A = K rows from LDS, B = Q (registers)
-//   O^T[dv][query] += V^T P^T    A = V^T rows from LDS, B = P (registers)
-// Computing the transposed products puts one query per lane column, so the
-// running max and sum are per-lane scalars (one cross-lane step, lane ^ 32),
-// and the accumulator layout of S^T is exactly the B-operand layout P needs
-// for the second product: P never leaves registers. V^T is stored in LDS with
-// keys permuted inside each group of 16 so that a lane's 8 keys are one
+//   S^T[key][query] = K Q^T      A = K (LDS), B = Q (registers, loaded once)
+//   O^T[dv][query] += V^T P^T    A = V^T (LDS), B = P (registers)
+// With the transposed products each lane column is one query, so the running
+// max and sum are per-lane scalars, and the S^T accumulator is already the
+// B operand P of the second product: P never leaves registers.
+//
+// Operand reads. An MFMA operand needs 8 consecutive reduction-index values
+// per lane. Where the LDS tile has the other index contiguous (K from NCHW
+// channel rows, V from [n, D] rows), the operand comes from two
+// ds_read_b64_tr_b16: inside each 16-lane group, lane i receives element i%4 of
+// the 8 bytes addressed by lane 4r + i/4, for r = 0..3 -- a 4x16 transpose.
+// The rows of S^T are also permuted (row 8h + 4g + e of each 16-row half holds
+// key 8g + 4h + e): the accumulator rows a lane holds for one 16-key step are
+// then 8 consecutive keys, so the V^T operand from NCHW channel rows is one
 // 16-byte read.
 //
-// Input layouts: "packed" ([BH, n, D] q/k/v, the layout PsaPackQkv writes) or
-// "NCHW" (the QKV conv output itself: Q, K, V channel rows of N pixels, so K
-// is transposed on its way into LDS and V is not). Softmax runs in base 2
-// with scale*log2(e) folded into one multiply-add; P is rounded to bf16 for
-// the PV product and the row sum adds the same rounded values.
+// Softmax runs in base 2 with scale*log2(e) folded into one multiply-add; the
+// running max is only moved when a tile's max exceeds it by more than 8 (so
+// P <= 2^8), which skips most rescales of O. P is rounded to bf16 for the PV
+// product and the row sum adds the same rounded values.
 #include <math.h>
 
 #include "psa_device.hpp"
@@ -36,7 +43,14 @@ namespace psa {
 namespace {
 
 constexpr int kBN = 64;   // keys per tile
-constexpr int kPad = 8;   // bf16 elements of padding per LDS row (breaks bank conflicts)
+constexpr int kPad = 8;   // bf16 elements of padding per LDS row (spreads banks)
+
+#ifndef PSA_LAZY_RESCALE
+#define PSA_LAZY_RESCALE 1
+#endif
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 struct FwdArgs {
   const uint16_t* q;   // packed: [BH, n_q, KD]; NCHW: the qkv tensor
@@ -79,175 +93,127 @@ __device__ __forceinline__ u32x4 gather8(const uint16_t* p, int64_t stride, int 
   return r;
 }
 
-// 8x8 transpose of 16-bit elements held as 8 rows of 16 bytes.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = in[2 * w][c >> 1];
-      const uint32_t hi = in[2 * w + 1][c >> 1];
-      out[c][w] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-  }
+// Two ds_read_b64_tr_b16 (rows p[0..3] and p[4*row..]) forming one 8-value operand.
+__device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* p, int row) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * row));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
 }
 
-// Writes 8 consecutive keys (8*mb .. 8*mb+7 of the tile) of one V^T row into
-// their permuted LDS positions: inside each group of 16 keys, key kappa goes
-// to 8*((kappa/4)%2) + 4*(kappa/8) + kappa%4.
-__device__ __forceinline__ void store_vt8(uint16_t* vt_row, int mb, u32x4 v) {
-  const int base = (mb >> 1) * 16 + (mb & 1) * 4;
-  *reinterpret_cast<u32x2*>(vt_row + base) = u32x2{v[0], v[1]};
-  *reinterpret_cast<u32x2*>(vt_row + base + 8) = u32x2{v[2], v[3]};
+// Key held by S^T row rho (0..31) of a 32-key block: 8h + 4g + e -> 8g + 4h + e
+// inside each 16-row half.
+__device__ __forceinline__ int key_of_row(int rho) {
+  return (rho & 16) | ((rho & 4) << 1) | ((rho & 8) >> 1) | (rho & 3);
 }
 
-template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves>
-struct FwdTile {
+// Column offset (in keys) a 16-lane group's source lane s supplies for the
+// transposed K read, so that output lane i receives key key_of_row(i).
+__device__ __forceinline__ int tr_key_col(int s) { return ((s & 1) << 3) | ((s & 2) << 1); }
+
+template <int KD, int DV, bool kNCHW, int kWaves>
+struct FwdCfg {
   static constexpr int NT = kWaves * 64;
-  static constexpr int DVP = DV < 32 ? 32 : DV;        // V^T rows (padded to one MFMA block)
-  static constexpr int KSTR = KD + kPad;               // LDS row stride of K (keys x d)
-  static constexpr int VSTR = kBN + kPad;              // LDS row stride of V^T (dv x keys)
-  static constexpr int K_ELEMS = kBN * KSTR;
-  static constexpr int V_ELEMS = DVP * VSTR;
+  static constexpr int BM = 32 * kWaves;
+  static constexpr int DVP = DV < 32 ? 32 : DV;            // O^T rows (one MFMA block minimum)
+  // NCHW: K as [KD][keys], V as [DV][keys]. packed: K as [keys][KD], V as [keys][DVP].
+  static constexpr int KROW = kNCHW ? kBN + kPad : KD + kPad;
+  static constexpr int VROW = kNCHW ? kBN + kPad : DVP + kPad;
+  static constexpr int K_ROWS = kNCHW ? KD : kBN;
+  static constexpr int V_ROWS = kNCHW ? DV : kBN;
+  static constexpr int K_ELEMS = K_ROWS * KROW;
+  static constexpr int V_ELEMS = V_ROWS * VROW;
   static constexpr int BUF = K_ELEMS + V_ELEMS;
-  // Staging work per tile.
-  static constexpr int K_CHUNKS = kNCHW ? (KD / 8) * (kBN / 8) : kBN * KD / 8;  // 8x8 blocks or 16B rows
-  static constexpr int V_CHUNKS = kNCHW ? DV * kBN / 8 : (kBN / 8) * (DV / 8);  // 16B rows or 8x8 blocks
-  static constexpr int K_PER = kNCHW ? 1 : (K_CHUNKS + NT - 1) / NT;
-  static constexpr int V_PER = kNCHW ? (V_CHUNKS + NT - 1) / NT : 1;
-  static_assert(!kNCHW || K_CHUNKS <= NT, "one K block per thread");
-  static_assert(kNCHW || V_CHUNKS <= NT, "one V block per thread");
-  static constexpr int KREG = kNCHW ? 8 : K_PER;
-  static constexpr int VREG = kNCHW ? V_PER : 8;
+  static constexpr int K_CPR = (kNCHW ? kBN : KD) / 8;     // 16-byte chunks per LDS row
+  static constexpr int V_CPR = (kNCHW ? kBN : DV) / 8;
+  static constexpr int K_CH = K_ROWS * K_CPR;
+  static constexpr int V_CH = V_ROWS * V_CPR;
+  static constexpr int PER = (K_CH + V_CH + NT - 1) / NT;  // chunks per thread per tile
+};
 
-  u32x4 kr[KREG];
-  u32x4 vr[VREG];
+// Global -> registers -> LDS staging of one key tile (K and V), 16-byte chunks.
+// Keys past n_k are clamped to real rows (finite data): their scores are
+// masked to -inf, so they contribute nothing. The unaligned NCHW variant
+// (N not a multiple of 8) gathers element by element and zero-fills instead.
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves>
+struct FwdStage {
+  using C = FwdCfg<KD, DV, kNCHW, kWaves>;
+  u32x4 r[C::PER];
 
-  // Global -> registers for key tile kt.
-  __device__ __forceinline__ void load(const FwdArgs& a, int bh, int kt, int tid, int N) {
+  __device__ __forceinline__ void load(const FwdArgs& a, int bh, int kt, int tid) {
     const int m0 = kt * kBN;
-    if constexpr (kNCHW) {
-      // K: 8x8 block (d-block db, key-block mb) of the [KD, N] channel rows.
-      if (tid < K_CHUNKS) {
-        const int db = tid / (kBN / 8), mb = tid % (kBN / 8);
-        const int m = m0 + mb * 8;
-        const uint16_t* src = a.k + (static_cast<int64_t>(bh) * 4 * KD + KD + db * 8) * N + m;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          if constexpr (kVecN)
-            kr[r] = (m < a.n_k) ? load16(src + static_cast<int64_t>(r) * N) : zero4();
-          else
-            kr[r] = gather8(src + static_cast<int64_t>(r) * N, 1, m, a.n_k);
-        }
-      }
-      // V: 16-byte runs of 8 keys along one of the DV channel rows.
-#pragma unroll
-      for (int i = 0; i < V_PER; ++i) {
-        const int c = tid + i * NT;
-        if (c < V_CHUNKS) {
-          const int dv = c / (kBN / 8), mb = c % (kBN / 8);
-          const int m = m0 + mb * 8;
-          const uint16_t* src = a.v + (static_cast<int64_t>(bh) * 4 * KD + 2 * KD + dv) * N + m;
-          if constexpr (kVecN)
-            vr[i] = (m < a.n_k) ? load16(src) : zero4();
-          else
-            vr[i] = gather8(src, 1, m, a.n_k);
-        }
-      }
-    } else {
-      // K: 16-byte pieces of key rows.
-#pragma unroll
-      for (int i = 0; i < K_PER; ++i) {
-        const int c = tid + i * NT;
-        if (c < K_CHUNKS) {
-          const int r = c / (KD / 8), cb = c % (KD / 8);
-          const int m = m0 + r;
-          kr[i] = (m < a.n_k) ? load16(a.k + (static_cast<int64_t>(bh) * a.n_k + m) * KD + cb * 8)
-                              : zero4();
-        }
-      }
-      // V: 8x8 block (key-block mb, dv-block db) of the [n_k, DV] rows.
-      if (tid < V_CHUNKS) {
-        const int mb = tid / (DV / 8), db = tid % (DV / 8);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int m = m0 + mb * 8 + r;
-          vr[r] = (m < a.n_k) ? load16(a.v + (static_cast<int64_t>(bh) * a.n_k + m) * DV + db * 8)
-                              : zero4();
-        }
+    for (int i = 0; i < C::PER; ++i) {
+      const int c = tid + i * C::NT;
+      if (c >= C::K_CH + C::V_CH) continue;
+      const bool is_k = c < C::K_CH;
+      const int cc = is_k ? c : c - C::K_CH;
+      const int row = cc / (is_k ? C::K_CPR : C::V_CPR);
+      const int col = cc - row * (is_k ? C::K_CPR : C::V_CPR);
+      if constexpr (kNCHW) {
+        const int N = a.n_k;
+        const int m = m0 + col * 8;
+        const int64_t ch = static_cast<int64_t>(bh) * 4 * KD + (is_k ? KD : 2 * KD) + row;
+        if constexpr (kVecN)
+          r[i] = load16(a.k + ch * N + (m < N ? m : N - 8));
+        else
+          r[i] = gather8(a.k + ch * N + m, 1, m, N);
+      } else {
+        int m = m0 + row;
+        m = m < a.n_k ? m : a.n_k - 1;
+        const int64_t rowi = static_cast<int64_t>(bh) * a.n_k + m;
+        r[i] = is_k ? load16(a.k + rowi * KD + col * 8) : load16(a.v + rowi * DV + col * 8);
       }
     }
   }
 
-  // Registers -> LDS buffer (K as [key][d], V^T as [dv][permuted key]).
   __device__ __forceinline__ void store(uint16_t* buf, int tid) const {
-    uint16_t* ks = buf;
-    uint16_t* vt = buf + K_ELEMS;
-    if constexpr (kNCHW) {
-      if (tid < K_CHUNKS) {
-        const int db = tid / (kBN / 8), mb = tid % (kBN / 8);
-        u32x4 t[8];
-        transpose8x8(kr, t);
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          *reinterpret_cast<u32x4*>(ks + (mb * 8 + c) * KSTR + db * 8) = t[c];
-      }
-#pragma unroll
-      for (int i = 0; i < V_PER; ++i) {
-        const int c = tid + i * NT;
-        if (c < V_CHUNKS) {
-          const int dv = c / (kBN / 8), mb = c % (kBN / 8);
-          store_vt8(vt + dv * VSTR, mb, vr[i]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < K_PER; ++i) {
-        const int c = tid + i * NT;
-        if (c < K_CHUNKS) {
-          const int r = c / (KD / 8), cb = c % (KD / 8);
-          *reinterpret_cast<u32x4*>(ks + r * KSTR + cb * 8) = kr[i];
-        }
-      }
-      if (tid < V_CHUNKS) {
-        const int mb = tid / (DV / 8), db = tid % (DV / 8);
-        u32x4 t[8];
-        transpose8x8(vr, t);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) store_vt8(vt + (db * 8 + c) * VSTR, mb, t[c]);
-      }
+    for (int i = 0; i < C::PER; ++i) {
+      const int c = tid + i * C::NT;
+      if (c >= C::K_CH + C::V_CH) continue;
+      const bool is_k = c < C::K_CH;
+      const int cc = is_k ? c : c - C::K_CH;
+      const int row = cc / (is_k ? C::K_CPR : C::V_CPR);
+      const int col = cc - row * (is_k ? C::K_CPR : C::V_CPR);
+      uint16_t* dst = is_k ? buf + row * C::KROW + col * 8 : buf + C::K_ELEMS + row * C::VROW + col * 8;
+      *reinterpret_cast<u32x4*>(dst) = r[i];
     }
   }
 };
 
-template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves>
-__global__ __launch_bounds__(kWaves * 64) void attn_fwd_bf16(FwdArgs a) {
-  using Tile = FwdTile<KD, DV, kNCHW, kVecN, kWaves>;
-  constexpr int NT = Tile::NT;
-  constexpr int BM = 32 * kWaves;
-  constexpr int DVP = Tile::DVP;
-  constexpr int NKB = kBN / 32;      // 32-key blocks per tile
-  constexpr int NKS = kBN / 16;      // 16-key MFMA steps per tile
-  constexpr int NDS = KD / 16;       // 16-wide d steps of Q K^T
-  constexpr int NDB = DVP / 32;      // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Tile::BUF];
+// kOcc: waves per SIMD the register allocation must allow (2 lets two
+// 4-wave workgroups share a CU, so one wave's softmax overlaps the other's MFMAs).
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
+__global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
+  using C = FwdCfg<KD, DV, kNCHW, kWaves>;
+  constexpr int NT = C::NT;
+  constexpr int BM = C::BM;
+  constexpr int NKB = kBN / 32;        // 32-key blocks per tile
+  constexpr int NKS = kBN / 16;        // 16-key MFMA steps per tile
+  constexpr int NDS = KD / 16;         // 16-wide d steps of K Q^T
+  constexpr int NDB = C::DVP / 32;     // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
-  const int g = lane >> 5;
+  const int g = lane >> 5;           // lane group of the MFMA layouts
+  const int i16 = lane & 15;         // lane inside its 16-lane group
+  const int t16 = (lane >> 4) & 1;   // which 16-row half of an operand block
   int bh, qt;
   tile_of_block(a.BH * a.q_tiles, a.q_tiles, bh, qt);
   const int N = a.n_k;   // NCHW: n_q == n_k == H*W
   const int q_row = qt * BM + wave * 32 + l32;
   const bool q_ok = q_row < a.n_q;
 
-  // Padded V^T rows (DV = 16) stay zero in both buffers.
-  if constexpr (DVP > DV) {
-    for (int e = tid; e < (DVP - DV) * Tile::VSTR; e += NT) {
-      smem[Tile::K_ELEMS + DV * Tile::VSTR + e] = 0;
-      smem[Tile::BUF + Tile::K_ELEMS + DV * Tile::VSTR + e] = 0;
+  // Packed V with DV = 16: columns 16..31 of every V row stay zero in both buffers.
+  if constexpr (!kNCHW && C::DVP > DV) {
+    for (int e = tid; e < kBN * (C::DVP - DV); e += NT) {
+      const int row = e / (C::DVP - DV), col = DV + e % (C::DVP - DV);
+      smem[C::K_ELEMS + row * C::VROW + col] = 0;
+      smem[C::BUF + C::K_ELEMS + row * C::VROW + col] = 0;
     }
   }
 
@@ -293,21 +259,21 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_bf16(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
   float m_run = -INFINITY;   // running max of scale*log2(e)*S
-  float l_run = 0.0f;        // this lane's part of the running sum (keys of lane group g)
+  float l_run = 0.0f;        // this lane's part of the running sum (its lane group's keys)
 
   const int n_tiles = (a.n_k + kBN - 1) / kBN;
-  Tile tile;
-  tile.load(a, bh, 0, tid, N);
-  tile.store(smem, tid);
+  FwdStage<KD, DV, kNCHW, kVecN, kWaves> stage;
+  stage.load(a, bh, 0, tid);
+  stage.store(smem, tid);
   __syncthreads();
 
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const uint16_t* ks = smem + (kt & 1) * Tile::BUF;
-    const uint16_t* vt = ks + Tile::K_ELEMS;
+    const uint16_t* ks = smem + (kt & 1) * C::BUF;
+    const uint16_t* vs = ks + C::K_ELEMS;
     const bool more = kt + 1 < n_tiles;
-    if (more) tile.load(a, bh, kt + 1, tid, N);
+    if (more) stage.load(a, bh, kt + 1, tid);
 
-    // S^T = K Q^T for the tile's keys.
+    // S^T = K Q^T for the tile's keys (rows permuted by key_of_row).
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -315,45 +281,56 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_bf16(FwdArgs a) {
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * Tile::KSTR + ds * 16 + g * 8);
+        bf16x8 kop;
+        if constexpr (kNCHW)
+          kop = lds_read_tr8(ks + (ds * 16 + 8 * g + (i16 >> 2)) * C::KROW + kb * 32 + 16 * t16 +
+                                 tr_key_col(i16 & 3), C::KROW);
+        else
+          kop = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + key_of_row(l32)) * C::KROW + ds * 16 + g * 8);
         sacc[kb] = mfma32x32x16(kop, qop[ds], sacc[kb]);
       }
     }
-    // Keys past n_k (last tile only) get -inf.
+    // Keys past n_k (last tile only) get -inf. Element r of block kb holds
+    // key 32*kb + 16*(r/8) + 8*g + r%8 of the tile.
     if ((kt + 1) * kBN > a.n_k) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt * kBN + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const int key = kt * kBN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
           if (key >= a.n_k) sacc[kb][r] = -INFINITY;
         }
     }
 
-    // Online softmax: new running max, rescale, P = 2^(c*S - m).
+    // Online softmax: running max, rescale, P = 2^(c*S - m).
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * a.c);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    const float m_tile = mx * a.c;
+#if PSA_LAZY_RESCALE
+    if (__any(m_tile > m_run + 8.0f)) {
+#else
+    {
+#endif
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
 
     bf16x8 pop[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -m_new));
-        pop[s][j] = static_cast<__bf16>(p);
-      }
+      for (int j = 0; j < 8; ++j)
+        pop[s][j] = static_cast<__bf16>(fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -m_run)));
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         const bf16x2 pp = {pop[s][j], pop[s][j + 1]};
@@ -361,16 +338,21 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_bf16(FwdArgs a) {
       }
     }
 
-    // O^T += V^T P^T.
+    // O^T += V^T P^T: step s covers keys 16s + 8g + j of the tile in this lane's P.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vt + (db * 32 + l32) * Tile::VSTR + s * 16 + g * 8);
+        bf16x8 vop;
+        if constexpr (kNCHW)
+          vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW + s * 16 + g * 8);
+        else
+          vop = lds_read_tr8(vs + (s * 16 + 8 * g + (i16 >> 2)) * C::VROW + db * 32 + 16 * t16 + 4 * (i16 & 3),
+                             C::VROW);
         oacc[db] = mfma32x32x16(vop, pop[s], oacc[db]);
       }
 
-    if (more) tile.store(smem + ((kt + 1) & 1) * Tile::BUF, tid);
+    if (more) stage.store(smem + ((kt + 1) & 1) * C::BUF, tid);
     __syncthreads();
   }
 
@@ -494,12 +476,14 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
 template <int KD, int DV, bool kNCHW, int kWaves>
 hipError_t run_bf16(FwdArgs a, bool vec_n, hipStream_t stream) {
   constexpr int BM = 32 * kWaves;
+  // Two workgroups per CU while both fit in LDS (160 KB) and 256 VGPRs per wave.
+  constexpr int kOcc = (KD <= 64 && 2 * 2 * FwdCfg<KD, DV, kNCHW, kWaves>::BUF * 2 <= 160 * 1024) ? 2 : 1;
   a.q_tiles = (a.n_q + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.BH) * a.q_tiles);
   if (vec_n)
-    attn_fwd_bf16<KD, DV, kNCHW, true, kWaves><<<grid, kWaves * 64, 0, stream>>>(a);
+    attn_fwd_bf16<KD, DV, kNCHW, true, kWaves, kOcc><<<grid, kWaves * 64, 0, stream>>>(a);
   else
-    attn_fwd_bf16<KD, DV, kNCHW, false, kWaves><<<grid, kWaves * 64, 0, stream>>>(a);
+    attn_fwd_bf16<KD, DV, kNCHW, false, kWaves, kOcc><<<grid, kWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -511,7 +495,10 @@ hipError_t run_f32(FwdArgsF32 a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-constexpr int kWavesFwd = 4;
+#ifndef PSA_FWD_WAVES
+#define PSA_FWD_WAVES 4
+#endif
+constexpr int kWavesFwd = PSA_FWD_WAVES;
 
 }  // namespace
 
