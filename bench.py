@@ -44,6 +44,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-step", action="store_true",
                     help="time only the fused step (for profiler runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy 3 times (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -127,6 +129,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        # A copy kernel of known size: reads and writes exactly 512 MiB per launch.
+        src = torch.ones(256 * 1024 * 1024, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes_read": src.numel() * 2,
+                          "calibration_copy_bytes_written": dst.numel() * 2}))
+        return
     w = I.WORKLOADS[WORKLOAD]
     qkv_cpu = I.make_workload_qkv(w)
     qkv = qkv_cpu.to(dev)
