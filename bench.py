@@ -44,6 +44,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-step", action="store_true",
                     help="time only the fused step (for profiler runs)")
+    ap.add_argument("--layout-only", action="store_true",
+                    help="only run pack, merge and extract a few times (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy 3 times (HBM counter calibration)")
     return ap.parse_args()
@@ -142,6 +144,15 @@ def main():
     w = I.WORKLOADS[WORKLOAD]
     qkv_cpu = I.make_workload_qkv(w)
     qkv = qkv_cpu.to(dev)
+    if args.layout_only:
+        packed = psa.psa_pack_qkv(qkv, w.heads, w.key_dim)
+        for _ in range(3):
+            psa.psa_pack_qkv(qkv, w.heads, w.key_dim, out=packed)
+            psa.psa_merge_attn(packed[:2], w.B, w.heads, w.key_dim, w.H, w.W)
+            psa.psa_extract_v(packed, w.B, w.heads, w.key_dim, w.H, w.W)
+        torch.cuda.synchronize()
+        print(json.dumps({"layout_only": True, "workload": w.name}))
+        return
     out = torch.empty((w.B, w.out_channels, w.H, w.W), dtype=torch.bfloat16, device=dev)
     vres = torch.empty_like(out)
     lse = torch.empty((w.BH, w.N), dtype=torch.float32, device=dev)
@@ -215,6 +226,9 @@ def components(torch, psa, I, w, qkv, args):
         "merge": (lambda i: psa.psa_merge_attn(packs[i % sets][:2], B, h, KD, H, W, out=outs[i % sets]), 2 * e_out * elt),
         "extract": (lambda i: psa.psa_extract_v(packs[i % sets], B, h, KD, H, W, out=outs[i % sets]), 2 * e_out * elt),
     }
+    # A plain device copy of the qkv tensor (same bytes as pack) as the practical reference.
+    copies = [torch.empty_like(qkv) for _ in range(sets)]
+    layout["device_copy_same_size_as_pack"] = (lambda i: copies[i % sets].copy_(qkvs[i % sets]), 2 * e_qkv * elt)
     for name, (fn, nbytes) in layout.items():
         avg, best, _ = time_events(fn, steps, warm, torch)
         gbps = nbytes / (avg * 1e-3) / 1e9

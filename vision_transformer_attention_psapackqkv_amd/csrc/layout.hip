@@ -13,14 +13,18 @@
 // laid out with the d-block index fastest, so every load instruction of a
 // wave covers whole 128-byte runs of NCHW rows and every store instruction
 // whole packed rows. No LDS is needed. Rows whose start is not 16-byte
-// aligned (N not a multiple of VEC) take a scalar kernel instead.
+// aligned (N not a multiple of VEC) take a scalar kernel instead. Measured on
+// MI355X at the 80x80 map, 256-thread workgroups suit pack and 128-thread
+// workgroups suit merge and extract (both above a plain device copy).
 #include "psa_device.hpp"
 #include "psa_launch.hpp"
 
 namespace psa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;            // scalar kernel
+constexpr int kThreadsToRows = 256;      // pack
+constexpr int kThreadsToNchw = 128;      // merge, extract
 
 // 8x8 transpose of 16-bit elements: in[r] holds row r (8 elements, two per
 // 32-bit word, element 2w in the low half of word w); out[c] receives column c.
@@ -63,13 +67,13 @@ __device__ __forceinline__ void slab_offsets(const SlabGeom& g, int t, int64_t& 
 
 // kToRows = true: NCHW [KD, N] slabs -> packed [N, KD] slabs (pack).
 // kToRows = false: packed [N, KD] slabs -> NCHW [KD, N] slabs (merge, extract).
-template <int kEltBytes, bool kToRows>
-__global__ __launch_bounds__(kThreads) void transpose_slabs_vec(const void* __restrict__ src_v,
-                                                                void* __restrict__ dst_v,
-                                                                SlabGeom g, int tiles_per_slab) {
+template <int kEltBytes, bool kToRows, int kTh = kToRows ? kThreadsToRows : kThreadsToNchw>
+__global__ __launch_bounds__(kTh) void transpose_slabs_vec(const void* __restrict__ src_v,
+                                                           void* __restrict__ dst_v,
+                                                           SlabGeom g, int tiles_per_slab) {
   constexpr int VEC = 16 / kEltBytes;
   const int DB = g.KD / VEC;             // d-blocks per row of the packed side
-  const int NBW = kThreads / DB;         // n-blocks per workgroup
+  const int NBW = kTh / DB;              // n-blocks per workgroup
   const int t = blockIdx.x / tiles_per_slab;
   const int tile = blockIdx.x - t * tiles_per_slab;
   const int db = threadIdx.x % DB;
@@ -126,13 +130,14 @@ hipError_t launch_transpose(const void* src, void* dst, SlabGeom g, int elt_byte
   const int n_slabs = g.BH * g.slots;
   const int vec = 16 / elt_bytes;
   if (g.N % vec == 0) {
-    const int nbw = kThreads / (g.KD / vec);
+    constexpr int th = kToRows ? kThreadsToRows : kThreadsToNchw;
+    const int nbw = th / (g.KD / vec);
     const int tiles = (g.N / vec + nbw - 1) / nbw;
     const dim3 grid(static_cast<unsigned>(n_slabs) * tiles);
     if (elt_bytes == 2)
-      transpose_slabs_vec<2, kToRows><<<grid, kThreads, 0, stream>>>(src, dst, g, tiles);
+      transpose_slabs_vec<2, kToRows><<<grid, th, 0, stream>>>(src, dst, g, tiles);
     else
-      transpose_slabs_vec<4, kToRows><<<grid, kThreads, 0, stream>>>(src, dst, g, tiles);
+      transpose_slabs_vec<4, kToRows><<<grid, th, 0, stream>>>(src, dst, g, tiles);
   } else {
     const int64_t per_slab = static_cast<int64_t>(g.N) * g.KD;
     const int tiles = static_cast<int>((per_slab + kThreads - 1) / kThreads);
