@@ -101,6 +101,21 @@ __device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* p, int row) {
   return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
 }
 
+#ifndef PSA_USE_PERMLANE
+#define PSA_USE_PERMLANE 1
+#endif
+// Value of x held by lane ^ 32 (g = lane / 32).
+__device__ __forceinline__ float lane_xor32(float x, int g) {
+#if PSA_USE_PERMLANE
+  const u32x2 sw = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
+      __builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false));
+  return __builtin_bit_cast(float, g ? sw[0] : sw[1]);
+#else
+  (void)g;
+  return __shfl_xor(x, 32);
+#endif
+}
+
 // Key held by S^T row rho (0..31) of a 32-key block: 8h + 4g + e -> 8g + 4h + e
 // inside each 16-row half.
 __device__ __forceinline__ int key_of_row(int rho) {
@@ -111,14 +126,16 @@ __device__ __forceinline__ int key_of_row(int rho) {
 // transposed K read, so that output lane i receives key key_of_row(i).
 __device__ __forceinline__ int tr_key_col(int s) { return ((s & 1) << 3) | ((s & 2) << 1); }
 
-template <int KD, int DV, bool kNCHW, int kWaves>
+template <int KD, int DV, bool kNCHW, int kWaves, int kQB, bool kDirect = false>
 struct FwdCfg {
   static constexpr int NT = kWaves * 64;
-  static constexpr int BM = 32 * kWaves;
+  static constexpr int BM = 32 * kQB * kWaves;   // queries per workgroup
   static constexpr int DVP = DV < 32 ? 32 : DV;            // O^T rows (one MFMA block minimum)
   // NCHW: K as [KD][keys], V as [DV][keys]. packed: K as [keys][KD], V as [keys][DVP].
-  static constexpr int KROW = kNCHW ? kBN + kPad : KD + kPad;
-  static constexpr int VROW = kNCHW ? kBN + kPad : DVP + kPad;
+  // Direct (global -> LDS) staging writes whole 1 KB runs, so its rows are unpadded.
+  static constexpr int PAD = kDirect ? 0 : kPad;
+  static constexpr int KROW = kNCHW ? kBN + PAD : KD + PAD;
+  static constexpr int VROW = kNCHW ? kBN + PAD : DVP + PAD;
   static constexpr int K_ROWS = kNCHW ? KD : kBN;
   static constexpr int V_ROWS = kNCHW ? DV : kBN;
   static constexpr int K_ELEMS = K_ROWS * KROW;
@@ -131,13 +148,52 @@ struct FwdCfg {
   static constexpr int PER = (K_CH + V_CH + NT - 1) / NT;  // chunks per thread per tile
 };
 
+// Position of 16-byte chunk c (8 keys) of V row dv in the unpadded, directly
+// staged V tile: an XOR swizzle that puts the 16 rows read together by one
+// 16-byte-per-lane instruction on 16 different bank groups.
+__device__ __forceinline__ int v_chunk_pos(int dv, int c) { return c ^ ((dv >> 1) & 7); }
+
+// Direct global -> LDS staging of one NCHW key tile (N a multiple of 8): each
+// wave instruction (global_load_lds_dwordx4) fills 64 consecutive 16-byte LDS
+// chunks, lane i the i-th; lanes pick which global chunk to fetch, which is
+// how the V swizzle is applied. No registers and no LDS write instructions;
+// the wave waits with vmcnt before the barrier that publishes the tile.
+template <int KD, int DV, int kWaves>
+struct FwdStageDirect {
+  static constexpr int K_BLOCKS = KD * (kBN / 8) / 64;     // 1 KB blocks of K
+  static constexpr int V_BLOCKS = DV * (kBN / 8) / 64;     // 1 KB blocks of V
+  static constexpr int BLOCKS = K_BLOCKS + V_BLOCKS;
+  static_assert(KD * (kBN / 8) % 64 == 0 && DV * (kBN / 8) % 64 == 0, "whole 1 KB blocks");
+
+  __device__ __forceinline__ void issue(const FwdArgs& a, int bh, int kt, int wave, int lane,
+                                        uint16_t* buf) const {
+    const int N = a.n_k;
+    const int m0 = kt * kBN;
+#pragma unroll
+    for (int i = 0; i < (BLOCKS + kWaves - 1) / kWaves; ++i) {
+      const int b = wave + i * kWaves;
+      if (b >= BLOCKS) break;
+      const int p = b * 64 + lane;                 // LDS chunk this lane fills
+      const bool is_k = b < K_BLOCKS;
+      const int q = is_k ? p : p - K_BLOCKS * 64;
+      const int row = q >> 3;                      // d (K) or dv (V)
+      const int c = is_k ? (q & 7) : v_chunk_pos(row, q & 7);
+      int m = m0 + c * 8;
+      m = m < N ? m : N - 8;                       // keys past n_k: real data, masked later
+      const int64_t ch = static_cast<int64_t>(bh) * 4 * KD + (is_k ? KD : 2 * KD) + row;
+      __builtin_amdgcn_global_load_lds(a.k + ch * N + m,
+                                       (__attribute__((address_space(3))) void*)(buf + b * 512), 16, 0, 0);
+    }
+  }
+};
+
 // Global -> registers -> LDS staging of one key tile (K and V), 16-byte chunks.
 // Keys past n_k are clamped to real rows (finite data): their scores are
 // masked to -inf, so they contribute nothing. The unaligned NCHW variant
 // (N not a multiple of 8) gathers element by element and zero-fills instead.
-template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves>
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kQB>
 struct FwdStage {
-  using C = FwdCfg<KD, DV, kNCHW, kWaves>;
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, kQB>;
   u32x4 r[C::PER];
 
   __device__ __forceinline__ void load(const FwdArgs& a, int bh, int kt, int tid) {
@@ -182,11 +238,14 @@ struct FwdStage {
   }
 };
 
-// kOcc: waves per SIMD the register allocation must allow (2 lets two
-// 4-wave workgroups share a CU, so one wave's softmax overlaps the other's MFMAs).
-template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
+// kQB: 32-query blocks per wave. With two, every K and V operand read from LDS
+// feeds two MFMAs (the LDS traffic per flop halves) and the two softmax chains
+// are independent work the wave interleaves with its MFMAs.
+// kOcc: waves per SIMD the register allocation must allow.
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kQB, int kOcc>
 __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
-  using C = FwdCfg<KD, DV, kNCHW, kWaves>;
+  constexpr bool kDirect = kNCHW && kVecN;   // direct global -> LDS staging
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, kQB, kDirect>;
   constexpr int NT = C::NT;
   constexpr int BM = C::BM;
   constexpr int NKB = kBN / 32;        // 32-key blocks per tile
@@ -205,8 +264,13 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   int bh, qt;
   tile_of_block(a.BH * a.q_tiles, a.q_tiles, bh, qt);
   const int N = a.n_k;   // NCHW: n_q == n_k == H*W
-  const int q_row = qt * BM + wave * 32 + l32;
-  const bool q_ok = q_row < a.n_q;
+  int q_row[kQB];
+  bool q_ok[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    q_row[qb] = qt * BM + (wave * kQB + qb) * 32 + l32;
+    q_ok[qb] = q_row[qb] < a.n_q;
+  }
 
   // Packed V with DV = 16: columns 16..31 of every V row stay zero in both buffers.
   if constexpr (!kNCHW && C::DVP > DV) {
@@ -238,47 +302,68 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   }
 
   // This lane's Q operands: Q[q_row][16*ds + 8*g + j], j = 0..7.
-  bf16x8 qop[NDS];
+  bf16x8 qop[kQB][NDS];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    u32x4 raw = zero4();
-    if (q_ok) {
-      if constexpr (kNCHW) {
-        const uint16_t* src = a.q + (static_cast<int64_t>(bh) * 4 * KD + ds * 16 + g * 8) * N + q_row;
-        raw = gather8(src, N, 0, 8);
-      } else {
-        raw = load16(a.q + (static_cast<int64_t>(bh) * a.n_q + q_row) * KD + ds * 16 + g * 8);
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      u32x4 raw = zero4();
+      if (q_ok[qb]) {
+        if constexpr (kNCHW) {
+          const uint16_t* src = a.q + (static_cast<int64_t>(bh) * 4 * KD + ds * 16 + g * 8) * N + q_row[qb];
+          raw = gather8(src, N, 0, 8);
+        } else {
+          raw = load16(a.q + (static_cast<int64_t>(bh) * a.n_q + q_row[qb]) * KD + ds * 16 + g * 8);
+        }
       }
+      qop[qb][ds] = as_bf16x8(raw);
     }
-    qop[ds] = as_bf16x8(raw);
+
+  f32x16 oacc[kQB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
+  float m_run[kQB], l_run[kQB];   // running max of scale*log2(e)*S; this lane's part of the sum
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
   }
 
-  f32x16 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-  float m_run = -INFINITY;   // running max of scale*log2(e)*S
-  float l_run = 0.0f;        // this lane's part of the running sum (its lane group's keys)
-
   const int n_tiles = (a.n_k + kBN - 1) / kBN;
-  FwdStage<KD, DV, kNCHW, kVecN, kWaves> stage;
-  stage.load(a, bh, 0, tid);
-  stage.store(smem, tid);
+  FwdStage<KD, DV, kNCHW, kVecN, kWaves, kQB> stage;
+  FwdStageDirect<KD, DV, kWaves> dstage;
+  if constexpr (kDirect) {
+    dstage.issue(a, bh, 0, wave, lane, smem);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    stage.load(a, bh, 0, tid);
+    stage.store(smem, tid);
+  }
   __syncthreads();
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const uint16_t* ks = smem + (kt & 1) * C::BUF;
     const uint16_t* vs = ks + C::K_ELEMS;
     const bool more = kt + 1 < n_tiles;
-    if (more) stage.load(a, bh, kt + 1, tid);
+    if constexpr (kDirect) {
+      if (more) dstage.issue(a, bh, kt + 1, wave, lane, smem + ((kt + 1) & 1) * C::BUF);
+    } else {
+      if (more) stage.load(a, bh, kt + 1, tid);
+    }
 
-    // S^T = K Q^T for the tile's keys (rows permuted by key_of_row).
-    f32x16 sacc[NKB];
+    // S^T = K Q^T for the tile's keys (rows permuted by key_of_row); one K
+    // operand read serves every query block.
+    f32x16 sacc[kQB][NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.0f;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         bf16x8 kop;
@@ -287,79 +372,97 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
                                  tr_key_col(i16 & 3), C::KROW);
         else
           kop = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + key_of_row(l32)) * C::KROW + ds * 16 + g * 8);
-        sacc[kb] = mfma32x32x16(kop, qop[ds], sacc[kb]);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) sacc[qb][kb] = mfma32x32x16(kop, qop[qb][ds], sacc[qb][kb]);
       }
     }
     // Keys past n_k (last tile only) get -inf. Element r of block kb holds
     // key 32*kb + 16*(r/8) + 8*g + r%8 of the tile.
     if ((kt + 1) * kBN > a.n_k) {
 #pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt * kBN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+            if (key >= a.n_k) sacc[qb][kb][r] = -INFINITY;
+          }
+    }
+
+    // Online softmax per query block: running max, rescale, P = 2^(c*S - m).
+    bf16x8 pop[kQB][NKS];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      float mx = sacc[qb][0][0];
+#pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * kBN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (key >= a.n_k) sacc[kb][r] = -INFINITY;
-        }
-    }
-
-    // Online softmax: running max, rescale, P = 2^(c*S - m).
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_tile = mx * a.c;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
+      mx = fmaxf(mx, lane_xor32(mx, g));
+      const float m_tile = mx * a.c;
 #if PSA_LAZY_RESCALE
-    if (__any(m_tile > m_run + 8.0f)) {
+      // The running max only moves when some lane's tile max exceeds it by
+      // more than 8 (log2 units): until then P <= 2^8, harmless in fp32 and bf16.
+      if (__any(m_tile > m_run[qb] + 8.0f)) {
 #else
-    {
+      {
 #endif
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+        const float m_new = fmaxf(m_run[qb], m_tile);
+        const float alpha = fast_exp2(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-
-    bf16x8 pop[NKS];
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+      }
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
+      for (int s = 0; s < NKS; ++s) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        pop[s][j] = static_cast<__bf16>(fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -m_run)));
+        for (int j = 0; j < 8; ++j)
+          pop[qb][s][j] = static_cast<__bf16>(fast_exp2(fmaf(sacc[qb][s >> 1][8 * (s & 1) + j], a.c, -m_run[qb])));
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const bf16x2 pp = {pop[s][j], pop[s][j + 1]};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l_run, false);
+        for (int j = 0; j < 8; j += 2) {
+          const bf16x2 pp = {pop[qb][s][j], pop[qb][s][j + 1]};
+          l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l_run[qb], false);
+        }
       }
     }
 
-    // O^T += V^T P^T: step s covers keys 16s + 8g + j of the tile in this lane's P.
+    // O^T += V^T P^T: step s covers keys 16s + 8g + j of the tile in this lane's P;
+    // one V operand read serves every query block.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         bf16x8 vop;
-        if constexpr (kNCHW)
+        if constexpr (kDirect)
+          vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW +
+                                                 v_chunk_pos(db * 32 + l32, 2 * s + g) * 8);
+        else if constexpr (kNCHW)
           vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW + s * 16 + g * 8);
         else
           vop = lds_read_tr8(vs + (s * 16 + 8 * g + (i16 >> 2)) * C::VROW + db * 32 + 16 * t16 + 4 * (i16 & 3),
                              C::VROW);
-        oacc[db] = mfma32x32x16(vop, pop[s], oacc[db]);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) oacc[qb][db] = mfma32x32x16(vop, pop[qb][s], oacc[qb][db]);
       }
 
-    if (more) stage.store(smem + ((kt + 1) & 1) * C::BUF, tid);
+    if constexpr (kDirect) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of tile kt+1 landed
+    } else {
+      if (more) stage.store(smem + ((kt + 1) & 1) * C::BUF, tid);
+    }
     __syncthreads();
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  if (q_ok) {
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float l_tot = l_run[qb] + lane_xor32(l_run[qb], g);
+    const float inv = 1.0f / l_tot;
+    if (!q_ok[qb]) continue;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -368,18 +471,18 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
         if (dv0 >= DV) continue;
         uint16_t h[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(oacc[db][4 * r4 + e] * inv);
+        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(oacc[qb][db][4 * r4 + e] * inv);
         if constexpr (kNCHW) {
-          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * DV + dv0) * N + q_row;
+          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * DV + dv0) * N + q_row[qb];
 #pragma unroll
           for (int e = 0; e < 4; ++e) dst[static_cast<int64_t>(e) * N] = h[e];
         } else {
-          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * a.n_q + q_row) * DV + dv0;
+          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * a.n_q + q_row[qb]) * DV + dv0;
           *reinterpret_cast<u32x2*>(dst) = u32x2{h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16)};
         }
       }
     if (a.lse != nullptr && g == 0)
-      a.lse[static_cast<int64_t>(bh) * a.n_q + q_row] = (m_run + log2f(l_tot)) * kLn2;
+      a.lse[static_cast<int64_t>(bh) * a.n_q + q_row[qb]] = (m_run[qb] + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -473,17 +576,27 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
 
 // ------------------------------------------------------------------ dispatch
 
+#ifndef PSA_QB
+#define PSA_QB 1
+#endif
+
 template <int KD, int DV, bool kNCHW, int kWaves>
 hipError_t run_bf16(FwdArgs a, bool vec_n, hipStream_t stream) {
-  constexpr int BM = 32 * kWaves;
-  // Two workgroups per CU while both fit in LDS (160 KB) and 256 VGPRs per wave.
-  constexpr int kOcc = (KD <= 64 && 2 * 2 * FwdCfg<KD, DV, kNCHW, kWaves>::BUF * 2 <= 160 * 1024) ? 2 : 1;
+  // Two 32-query blocks per wave (one wave per SIMD) where the registers allow;
+  // head dim 128 keeps one block per wave.
+  constexpr int kQB = KD <= 64 ? PSA_QB : 1;
+  constexpr int BM = 32 * kQB * kWaves;
+#ifdef PSA_FWD_OCC
+  constexpr int kOcc = KD <= 64 ? PSA_FWD_OCC : 1;
+#else
+  constexpr int kOcc = (kQB == 1 && KD <= 64 && 2 * 2 * FwdCfg<KD, DV, kNCHW, kWaves, kQB>::BUF * 2 <= 160 * 1024) ? 2 : 1;
+#endif
   a.q_tiles = (a.n_q + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.BH) * a.q_tiles);
   if (vec_n)
-    attn_fwd_bf16<KD, DV, kNCHW, true, kWaves, kOcc><<<grid, kWaves * 64, 0, stream>>>(a);
+    attn_fwd_bf16<KD, DV, kNCHW, true, kWaves, kQB, kOcc><<<grid, kWaves * 64, 0, stream>>>(a);
   else
-    attn_fwd_bf16<KD, DV, kNCHW, false, kWaves, kOcc><<<grid, kWaves * 64, 0, stream>>>(a);
+    attn_fwd_bf16<KD, DV, kNCHW, false, kWaves, kQB, kOcc><<<grid, kWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
