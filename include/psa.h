@@ -17,9 +17,10 @@
  *
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers to contiguous row-major buffers, 16-byte
- *    aligned. The caller owns every buffer; the library allocates nothing,
- *    keeps no state except a thread-local error string, and never
- *    synchronizes.
+ *    aligned. The caller owns every buffer; the library allocates nothing and
+ *    never synchronizes. Its only state is a thread-local error string and a
+ *    per-process cache of device properties (CU count of each device, the
+ *    occupancy of each kernel) that launches are sized with.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued asynchronously on it.
  *  - Outputs are overwritten, never accumulated into. Inputs are read only.
@@ -44,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PSA_ABI_VERSION 1
+#define PSA_ABI_VERSION 2
 
 typedef enum psa_dtype {
   PSA_F32 = 0,
@@ -92,6 +93,24 @@ psa_status psa_merge_attn(const void* o2, void* out_nchw, int B, int heads, int 
                           int H, int W, psa_dtype dtype, void* stream);
 
 /*
+ * Forward workspaces (fa2_fwd, psa_attention_fwd). A bf16 forward launch
+ * gives each workgroup one tile of queries. When the tiles fill the device's
+ * resident workgroup slots a whole number of times plus a short last round,
+ * that round would run on a few CUs while the rest idle; with a workspace the
+ * launch instead cuts the last round's tiles into key-range pieces, spreads
+ * them over the whole device and merges them with the log-sum-exp weights of
+ * the online softmax (a second, small kernel on the same stream). The
+ * *_workspace_bytes functions give the bytes this needs on the CURRENT device
+ * (0: these sizes do not split; also 0 for PSA_F32 and for invalid sizes).
+ * workspace may be NULL, or smaller than that: the launch then runs unsplit,
+ * with the same results to within rounding. A workspace must be 16-byte
+ * aligned and must not overlap any other argument; its contents on entry do
+ * not matter and on return are unspecified. Two launches in flight at once
+ * must not share one.
+ */
+size_t fa2_fwd_workspace_bytes(int BH, int n_q, int n_k, int head_dim, psa_dtype dtype);
+
+/*
  * Flash Attention 2 forward (vision-rs book, "Custom Kernels", "Flash
  * Attention 2": online softmax over [BATCH*N_HEADS, N_CTX, HEAD_DIM] tensors;
  * the n_q x n_k score matrix is never stored):
@@ -99,11 +118,12 @@ psa_status psa_merge_attn(const void* o2, void* out_nchw, int B, int heads, int 
  *   lse[bh][n]  = ln sum_m exp(scale * q[bh][n] . k[bh][m])      (natural log)
  * q: [BH, n_q, head_dim]; k, v: [BH, n_k, head_dim]; o: [BH, n_q, head_dim];
  * lse: [BH, n_q] float32, or NULL to skip it. No mask, no dropout, no bias.
- * scale must be finite and > 0.
+ * scale must be finite and > 0. workspace / workspace_bytes: see "Forward
+ * workspaces" above (NULL allowed).
  */
 psa_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int BH, int n_q, int n_k, int head_dim, float scale, psa_dtype dtype,
-                   void* stream);
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Flash Attention 2 backward: the dQ kernel and the dK/dV kernel are separate
@@ -135,10 +155,16 @@ size_t fa2_bwd_workspace_bytes(int BH, int n_q);
  * v_nchw: [B, 2*h*KD, H, W] V residual exactly as psa_extract_v writes it, or
  * NULL to skip it. lse: [B*h, H*W] float32, or NULL.
  * scale must be finite and > 0 (the PSA block uses key_dim ** -0.5).
+ * workspace / workspace_bytes: see "Forward workspaces" above (NULL allowed).
  */
 psa_status psa_attention_fwd(const void* qkv_nchw, void* out_nchw, void* v_nchw, float* lse,
                              int B, int heads, int key_dim, int H, int W, float scale,
-                             psa_dtype dtype, void* stream);
+                             psa_dtype dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace bytes for psa_attention_fwd; see "Forward workspaces" above. */
+size_t psa_attention_fwd_workspace_bytes(int B, int heads, int key_dim, int H, int W,
+                                         psa_dtype dtype);
 
 /* Message of the last error on this thread ("" after a success). */
 const char* psa_last_error(void);

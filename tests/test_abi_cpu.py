@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     assert names == set(_binding.SIGNATURES), names ^ set(_binding.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.psa_abi_version() == 1
+    assert lib.psa_abi_version() == 2
 
 
 def _status(fn, *args):
@@ -68,8 +68,9 @@ def test_layout_argument_errors(fn):
 
 
 def test_fa2_fwd_argument_errors():
-    def call(q=A, k=B_, v=C_, o=0xB0000000, lse=None, BH=2, nq=10, nk=12, D=64, s=0.125, dt=1):
-        return _status("fa2_fwd", q, k, v, o, lse, BH, nq, nk, D, ctypes.c_float(s), dt, None)
+    def call(q=A, k=B_, v=C_, o=0xB0000000, lse=None, BH=2, nq=10, nk=12, D=64, s=0.125, dt=1,
+             ws=None, wsb=0):
+        return _status("fa2_fwd", q, k, v, o, lse, BH, nq, nk, D, ctypes.c_float(s), dt, ws, wsb, None)
 
     assert call(q=None)[0] == 1
     assert call(o=None)[0] == 1
@@ -85,6 +86,12 @@ def test_fa2_fwd_argument_errors():
     assert call(lse=0xC0000004)[0] == 4
     assert call(o=A)[0] == 5           # output aliases q
     assert call(lse=B_ + 16)[0] == 5   # lse inside k
+    st, msg = call(ws=0xD0000008, wsb=4096)
+    assert st == 4 and "workspace" in msg
+    st, msg = call(ws=C_ + 64, wsb=4096)   # workspace inside v
+    assert st == 5 and "workspace" in msg
+    st, msg = call(ws=0xB0000000 - 1024, wsb=4096)   # workspace runs into o
+    assert st == 5 and "workspace" in msg
 
 
 def test_fa2_bwd_argument_errors():
@@ -111,8 +118,9 @@ def test_fa2_bwd_argument_errors():
 
 
 def test_fused_argument_errors():
-    def call(x=A, out=B_, v=None, lse=None, B=1, h=2, kd=64, H=5, W=5, s=0.125, dt=1):
-        return _status("psa_attention_fwd", x, out, v, lse, B, h, kd, H, W, ctypes.c_float(s), dt, None)
+    def call(x=A, out=B_, v=None, lse=None, B=1, h=2, kd=64, H=5, W=5, s=0.125, dt=1, ws=None, wsb=0):
+        return _status("psa_attention_fwd", x, out, v, lse, B, h, kd, H, W, ctypes.c_float(s), dt,
+                       ws, wsb, None)
 
     assert call(x=None)[0] == 1
     assert call(out=None)[0] == 1
@@ -123,6 +131,22 @@ def test_fused_argument_errors():
     assert call(v=B_)[0] == 5           # V residual aliases out
     st, msg = call(out=A + 16)
     assert st == 5 and msg.startswith("psa_attention_fwd")
+    assert call(ws=C_ + 4, wsb=64)[0] == 4
+    st, msg = call(ws=B_ + 32, wsb=64)   # workspace inside out
+    assert st == 5 and "workspace" in msg
+
+
+def test_forward_workspace_bytes_without_a_device():
+    """Invalid sizes and float32 ask for no workspace; without a GPU no launch is
+    sized, so no split is planned either."""
+    lib = psa.load_library()
+    assert lib.fa2_fwd_workspace_bytes(0, 10, 10, 64, 1) == 0
+    assert lib.fa2_fwd_workspace_bytes(2, 10, 10, 48, 1) == 0
+    assert lib.fa2_fwd_workspace_bytes(32, 6400, 6400, 64, 0) == 0
+    assert lib.fa2_fwd_workspace_bytes(2, 10, 10, 64, 9) == 0
+    assert lib.psa_attention_fwd_workspace_bytes(4, 8, 24, 80, 80, 1) == 0
+    assert lib.psa_attention_fwd_workspace_bytes(4, 8, 64, 80, 80, 0) == 0
+    assert lib.psa_attention_fwd_workspace_bytes(-1, 8, 64, 80, 80, 1) == 0
 
 
 def test_error_string_cleared_on_next_error_free_path():

@@ -144,3 +144,61 @@ def test_psa_fused_repeatable_and_matches_halves():
     lo_nchw = to_f64(o1).reshape(B * h, 2 * KD, H * W)[:, :KD].transpose(0, 2, 1)
     assert_attention_close(lo_nchw, to_f64(lo), "bf16", "fused lo half vs fa2_fwd")
     assert np.abs(to_f64(lse_lo) - to_f64(l1)).max() < 5e-3
+
+
+# Grids that leave a short partial last round of workgroups on a 256-CU gfx950
+# (80x80 maps at batch 2 and 4, key_dim 128 at batch 4, a 48x48 map with
+# key_dim 32 at batch 8): given a workspace, the launch cuts those last query
+# tiles into key-range pieces and merges them in a second kernel. Checked on
+# the first head and the last two (whose tiles are all in the last round),
+# every query row, and against the same launch run unsplit.
+TAIL_PSA = [
+    (2, 8, 64, 80, 80),
+    (4, 4, 128, 80, 80),
+    (8, 8, 32, 48, 48),
+]
+
+
+@pytest.mark.parametrize("shape", TAIL_PSA, ids=lambda s: "B{}h{}kd{}_{}x{}".format(*s))
+def test_psa_fused_tail_split(shape):
+    dev = device()
+    B, h, KD, H, W = shape
+    announce(f"psa_attention_fwd tail split B{B}h{h}kd{KD}_{H}x{W}")
+    nbytes = psa.psa_attention_fwd_workspace_bytes(B, h, KD, H, W)
+    assert nbytes > 0, "this grid is expected to split its last round on a 256-CU gfx950"
+    qkv = I.make_qkv(B, h, KD, H, W, seed=5 * B + KD + H)
+    x = qkv.to(dev)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out, vres, lse = psa.psa_attention_fwd(x, h, KD, workspace=ws)
+    sel = np.array([0, B * h - 2, B * h - 1])
+    _check_psa(qkv, B, h, KD, H, W, "bf16", out, vres, lse, bh_sel=sel)
+    # a second call on the same workspace gives the same bits
+    out2, _, lse2 = psa.psa_attention_fwd(x, h, KD, workspace=ws)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    # unsplit (no workspace, or 16 bytes short): the same bits either way, and close
+    # to the split run. The two differ only in how P is rounded to bf16 (each piece
+    # rounds against its own running max), so O within one bf16 step and LSE within
+    # 1e-3 (relative error of the row sum).
+    empty = torch.empty(0, dtype=torch.uint8, device=dev)
+    short = ws[: nbytes - 16]
+    o_none, _, l_none = psa.psa_attention_fwd(x, h, KD, workspace=empty)
+    o_short, _, l_short = psa.psa_attention_fwd(x, h, KD, workspace=short)
+    assert torch.equal(o_none, o_short) and torch.equal(l_none, l_short)
+    diff = (o_none.float() - out.float()).abs()
+    assert diff.max().item() <= 2.0 ** -7 * max(1.0, out.float().abs().max().item())
+    assert (l_none - lse).abs().max().item() < 1e-3
+
+
+def test_fa2_fwd_tail_split():
+    """FA2 forward on packed [BH, n, D] tensors whose grid leaves a short last round
+    (BH = 32, n = 6400, D = 64), checked on the last two batch-heads."""
+    dev = device()
+    BH, n, D = 32, 6400, 64
+    announce("fa2_fwd tail split BH32 n6400 d64")
+    assert psa.fa2_fwd_workspace_bytes(BH, n, n, D) > 0
+    q, k, v = I.make_attention_inputs(BH, n, n, D, seed=31)
+    o, lse = psa.fa2_fwd(q.to(dev), k.to(dev), v.to(dev))
+    sel = [BH - 2, BH - 1]
+    want_o, want_lse = O.attention(to_f64(q)[sel], to_f64(k)[sel], to_f64(v)[sel], D ** -0.5)
+    assert_attention_close(to_f64(o)[sel], want_o, "bf16", "fa2_fwd tail O")
+    assert_lse_close(to_f64(lse)[sel], want_lse, "bf16", "fa2_fwd tail")

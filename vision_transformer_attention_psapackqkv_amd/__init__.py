@@ -12,9 +12,11 @@ from ._binding import (  # noqa: F401
     default_scale,
     fa2_bwd,
     fa2_fwd,
+    fa2_fwd_workspace_bytes,
     load_library,
     psa_abi_version,
     psa_attention_fwd,
+    psa_attention_fwd_workspace_bytes,
     psa_extract_v,
     psa_merge_attn,
     psa_pack_qkv,

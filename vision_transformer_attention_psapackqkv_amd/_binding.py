@@ -25,10 +25,12 @@ SIGNATURES = {
     "psa_pack_qkv": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "psa_extract_v": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "psa_merge_attn": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
-    "fa2_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "fa2_fwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "fa2_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]),
     "fa2_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa2_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
-    "psa_attention_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "psa_attention_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]),
+    "psa_attention_fwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "psa_last_error": (ctypes.c_char_p, []),
     "psa_abi_version": (_I, []),
 }
@@ -129,8 +131,34 @@ def psa_merge_attn(o2, B, heads, key_dim, H, W, out=None):
     return _rows_to_nchw("psa_merge_attn", o2, 2, B, heads, key_dim, H, W, out)
 
 
-def fa2_fwd(q, k, v, scale=None, out=None, lse=None, want_lse=True):
-    """FA2 forward on ``[BH, n, D]`` tensors; returns ``(o, lse)`` (lse is None if not wanted)."""
+def _workspace(ws, nbytes, device):
+    """(pointer, bytes) of a forward workspace: a new one of ``nbytes`` if ``ws`` is None,
+    else the given tensor (an empty one runs the launch unsplit)."""
+    if ws is None:
+        if nbytes == 0:
+            return None, 0
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace")
+    return (ws.data_ptr() if ws.numel() else None), ws.numel() * ws.element_size()
+
+
+def fa2_fwd_workspace_bytes(BH, n_q, n_k, head_dim, dtype=torch.bfloat16):
+    """Workspace bytes that let fa2_fwd split the last round of its grid (0: no split)."""
+    code = PSA_BF16 if dtype == torch.bfloat16 else PSA_F32
+    return load_library().fa2_fwd_workspace_bytes(BH, n_q, n_k, head_dim, code)
+
+
+def psa_attention_fwd_workspace_bytes(B, heads, key_dim, H, W, dtype=torch.bfloat16):
+    """Workspace bytes that let psa_attention_fwd split the last round of its grid (0: no split)."""
+    code = PSA_BF16 if dtype == torch.bfloat16 else PSA_F32
+    return load_library().psa_attention_fwd_workspace_bytes(B, heads, key_dim, H, W, code)
+
+
+def fa2_fwd(q, k, v, scale=None, out=None, lse=None, want_lse=True, workspace=None):
+    """FA2 forward on ``[BH, n, D]`` tensors; returns ``(o, lse)`` (lse is None if not wanted).
+
+    ``workspace``: None allocates the bytes ``fa2_fwd_workspace_bytes`` asks for; a given
+    GPU tensor is used as is (an empty one runs the launch without the tail split)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n)
     BH, n_q, D = q.shape
@@ -142,8 +170,11 @@ def fa2_fwd(q, k, v, scale=None, out=None, lse=None, want_lse=True):
     if lse is None and want_lse:
         lse = torch.empty((BH, n_q), dtype=torch.float32, device=q.device)
     s = default_scale(D) if scale is None else float(scale)
-    _check(load_library().fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dev(out, "out").data_ptr(),
-                                  _ptr(lse), BH, n_q, n_k, D, s, _dtype_code(q), _stream(q)))
+    lib = load_library()
+    code = _dtype_code(q)
+    wp, wb = _workspace(workspace, lib.fa2_fwd_workspace_bytes(BH, n_q, n_k, D, code), q.device)
+    _check(lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dev(out, "out").data_ptr(),
+                       _ptr(lse), BH, n_q, n_k, D, s, code, wp, wb, _stream(q)))
     return out, lse
 
 
@@ -166,8 +197,10 @@ def fa2_bwd(q, k, v, o, dout, lse, scale=None, workspace=None):
 
 
 def psa_attention_fwd(qkv, heads, key_dim, scale=None, want_v=True, want_lse=True,
-                      out=None, v_out=None, lse=None):
-    """Fused PSA forward on NCHW ``qkv``; returns ``(out, v_residual, lse)`` (None where not wanted)."""
+                      out=None, v_out=None, lse=None, workspace=None):
+    """Fused PSA forward on NCHW ``qkv``; returns ``(out, v_residual, lse)`` (None where not wanted).
+
+    ``workspace`` as for :func:`fa2_fwd` (bytes from ``psa_attention_fwd_workspace_bytes``)."""
     _dev(qkv, "qkv")
     B, C, H, W = qkv.shape
     if C != 4 * heads * key_dim:
@@ -180,9 +213,12 @@ def psa_attention_fwd(qkv, heads, key_dim, scale=None, want_v=True, want_lse=Tru
     if lse is None and want_lse:
         lse = torch.empty((B * heads, H * W), dtype=torch.float32, device=qkv.device)
     s = default_scale(key_dim) if scale is None else float(scale)
-    _check(load_library().psa_attention_fwd(qkv.data_ptr(), _dev(out, "out").data_ptr(), _ptr(v_out),
-                                            _ptr(lse), B, heads, key_dim, H, W, s,
-                                            _dtype_code(qkv), _stream(qkv)))
+    lib = load_library()
+    code = _dtype_code(qkv)
+    wp, wb = _workspace(workspace, lib.psa_attention_fwd_workspace_bytes(B, heads, key_dim, H, W, code),
+                        qkv.device)
+    _check(lib.psa_attention_fwd(qkv.data_ptr(), _dev(out, "out").data_ptr(), _ptr(v_out),
+                                 _ptr(lse), B, heads, key_dim, H, W, s, code, wp, wb, _stream(qkv)))
     return out, v_out, lse
 
 

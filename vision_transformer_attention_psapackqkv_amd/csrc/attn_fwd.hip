@@ -9,9 +9,18 @@
 //
 // Work decomposition (ours, not the page's one-program-per-query-row): one
 // workgroup per (batch-head, tile of 32*kWaves queries); each wave owns 32
-// queries and walks all keys in tiles of 64, staged in LDS by plain 16-byte
-// copies in the tensors' own layout (double-buffered: the next tile's global
-// loads are in flight while the current tile is computed).
+// queries and walks all keys in tiles of 64, staged in LDS in the tensors' own
+// layout and double-buffered (the next tile's loads are in flight while the
+// current tile is computed). NCHW tiles with N a multiple of 8 go from global
+// memory straight into LDS (global_load_lds_dwordx4, no registers on the way);
+// the others pass through registers.
+//
+// Tail split: a grid rarely fills the chip's workgroup slots a whole number of
+// times, and the last partial round would run on a few CUs while the rest idle.
+// Those last query tiles are instead cut into key-range pieces, each an
+// ordinary workgroup that stores its unnormalised O^T with its running max and
+// sum; a small second kernel merges the pieces with the usual log-sum-exp
+// weights and writes those tiles' outputs.
 //
 // Per wave and key tile, on the matrix cores (v_mfma_f32_32x32x16_bf16):
 //   S^T[key][query] = K Q^T      A = K (LDS), B = Q (registers, loaded once)
@@ -43,11 +52,8 @@ namespace psa {
 namespace {
 
 constexpr int kBN = 64;   // keys per tile
+constexpr int kWavesFwd = 4;   // waves per workgroup, 32 queries each
 constexpr int kPad = 8;   // bf16 elements of padding per LDS row (spreads banks)
-
-#ifndef PSA_LAZY_RESCALE
-#define PSA_LAZY_RESCALE 1
-#endif
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -62,17 +68,37 @@ struct FwdArgs {
   int BH, n_q, n_k;
   int q_tiles;
   float c;             // scale * log2(e)
+  int full;            // workgroups [0, full) each own a whole query tile
+  int tail;            // query tiles split into key-range pieces (after them)
+  int splits;          // pieces per split tile
+  float* part;         // per piece: O^T [DV][BM] (unnormalised), m [BM], l [BM]
 };
 
-// blockIdx -> (bh, query tile). Workgroups are dispatched round-robin over the
-// 8 XCDs; this remap gives each XCD a contiguous run of logical tiles, so the
-// query tiles of one batch-head share an L2 and its K/V stay resident there.
-__device__ __forceinline__ void tile_of_block(int total, int q_tiles, int& bh, int& qt) {
-  const int i = blockIdx.x;
-  const int per = total / 8;
-  const int L = (i < per * 8) ? (i % 8) * per + i / 8 : i;
-  bh = L / q_tiles;
-  qt = L - bh * q_tiles;
+// Logical query tiles L = bh * q_tiles + qt in XCD-aware order. Workgroups are
+// dispatched round-robin over the 8 XCDs (block i runs on XCD i % 8), so XCD x
+// is given the contiguous run of tiles [x * per, (x + 1) * per): the query
+// tiles of a batch-head share one L2 and its K/V stay resident there. When
+// the tail is split, the split tiles are the last tail / 8 of every XCD's run
+// and their pieces are dispatched on that same XCD. (Grids whose tile counts
+// are not multiples of 8 use a plainer order.)
+__device__ __forceinline__ bool xcd_order(const FwdArgs& a) {
+  return (a.full + a.tail) % 8 == 0 && a.tail % 8 == 0;
+}
+
+// Tile of whole-tile workgroup i (i < full).
+__device__ __forceinline__ int full_tile(const FwdArgs& a, int i) {
+  if (xcd_order(a)) return (i % 8) * ((a.full + a.tail) / 8) + i / 8;
+  const int per = a.full / 8;
+  return (i < per * 8) ? (i % 8) * per + i / 8 : i;
+}
+
+// Tile of split tile s (0 <= s < tail); split tile s runs on XCD s % 8.
+__device__ __forceinline__ int split_tile(const FwdArgs& a, int s) {
+  if (xcd_order(a)) {
+    const int per = (a.full + a.tail) / 8;
+    return (s % 8) * per + (per - a.tail / 8) + s / 8;
+  }
+  return a.full + s;
 }
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
@@ -101,19 +127,13 @@ __device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* p, int row) {
   return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
 }
 
-#ifndef PSA_USE_PERMLANE
-#define PSA_USE_PERMLANE 1
-#endif
-// Value of x held by lane ^ 32 (g = lane / 32).
+// Value of x held by lane ^ 32 (g = lane / 32): one v_permlane32_swap, which
+// leaves the partner's value in the first result on the upper half-wave and
+// in the second on the lower.
 __device__ __forceinline__ float lane_xor32(float x, int g) {
-#if PSA_USE_PERMLANE
   const u32x2 sw = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
       __builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false));
   return __builtin_bit_cast(float, g ? sw[0] : sw[1]);
-#else
-  (void)g;
-  return __shfl_xor(x, 32);
-#endif
 }
 
 // Key held by S^T row rho (0..31) of a 32-key block: 8h + 4g + e -> 8g + 4h + e
@@ -126,10 +146,11 @@ __device__ __forceinline__ int key_of_row(int rho) {
 // transposed K read, so that output lane i receives key key_of_row(i).
 __device__ __forceinline__ int tr_key_col(int s) { return ((s & 1) << 3) | ((s & 2) << 1); }
 
-template <int KD, int DV, bool kNCHW, int kWaves, int kQB, bool kDirect = false>
+
+template <int KD, int DV, bool kNCHW, int kWaves, bool kDirect>
 struct FwdCfg {
   static constexpr int NT = kWaves * 64;
-  static constexpr int BM = 32 * kQB * kWaves;   // queries per workgroup
+  static constexpr int BM = 32 * kWaves;                   // queries per workgroup
   static constexpr int DVP = DV < 32 ? 32 : DV;            // O^T rows (one MFMA block minimum)
   // NCHW: K as [KD][keys], V as [DV][keys]. packed: K as [keys][KD], V as [keys][DVP].
   // Direct (global -> LDS) staging writes whole 1 KB runs, so its rows are unpadded.
@@ -146,7 +167,14 @@ struct FwdCfg {
   static constexpr int K_CH = K_ROWS * K_CPR;
   static constexpr int V_CH = V_ROWS * V_CPR;
   static constexpr int PER = (K_CH + V_CH + NT - 1) / NT;  // chunks per thread per tile
+  static constexpr int PART = (DV + 2) * BM;               // floats per split piece
 };
+
+// Tail split limits: at most kMaxSplits pieces per query tile, each of at
+// least kSplitMinTiles key tiles (shorter pieces do not repay their extra
+// partial-result traffic and the merge).
+constexpr int kMaxSplits = 6;
+constexpr int kSplitMinTiles = 16;
 
 // Position of 16-byte chunk c (8 keys) of V row dv in the unpadded, directly
 // staged V tile: an XOR swizzle that puts the 16 rows read together by one
@@ -191,9 +219,9 @@ struct FwdStageDirect {
 // Keys past n_k are clamped to real rows (finite data): their scores are
 // masked to -inf, so they contribute nothing. The unaligned NCHW variant
 // (N not a multiple of 8) gathers element by element and zero-fills instead.
-template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kQB>
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves>
 struct FwdStage {
-  using C = FwdCfg<KD, DV, kNCHW, kWaves, kQB>;
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, false>;
   u32x4 r[C::PER];
 
   __device__ __forceinline__ void load(const FwdArgs& a, int bh, int kt, int tid) {
@@ -238,14 +266,11 @@ struct FwdStage {
   }
 };
 
-// kQB: 32-query blocks per wave. With two, every K and V operand read from LDS
-// feeds two MFMAs (the LDS traffic per flop halves) and the two softmax chains
-// are independent work the wave interleaves with its MFMAs.
 // kOcc: waves per SIMD the register allocation must allow.
-template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kQB, int kOcc>
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
 __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   constexpr bool kDirect = kNCHW && kVecN;   // direct global -> LDS staging
-  using C = FwdCfg<KD, DV, kNCHW, kWaves, kQB, kDirect>;
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, kDirect>;
   constexpr int NT = C::NT;
   constexpr int BM = C::BM;
   constexpr int NKB = kBN / 32;        // 32-key blocks per tile
@@ -261,16 +286,33 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   const int g = lane >> 5;           // lane group of the MFMA layouts
   const int i16 = lane & 15;         // lane inside its 16-lane group
   const int t16 = (lane >> 4) & 1;   // which 16-row half of an operand block
-  int bh, qt;
-  tile_of_block(a.BH * a.q_tiles, a.q_tiles, bh, qt);
   const int N = a.n_k;   // NCHW: n_q == n_k == H*W
-  int q_row[kQB];
-  bool q_ok[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    q_row[qb] = qt * BM + (wave * kQB + qb) * 32 + l32;
-    q_ok[qb] = q_row[qb] < a.n_q;
+  const int n_tiles = (a.n_k + kBN - 1) / kBN;
+
+  // Work unit: a whole query tile, or key tiles [kt0, kt1) (piece `piece`) of
+  // split tile `split`.
+  int L, split = -1, piece = 0, kt0 = 0, kt1 = n_tiles;
+  const int i = blockIdx.x;
+  if (i < a.full) {
+    L = full_tile(a, i);
+  } else {
+    const int j = i - a.full;   // pieces of one split tile stay on one XCD
+    if (xcd_order(a)) {
+      const int local = j / 8;
+      split = (local / a.splits) * 8 + j % 8;
+      piece = local % a.splits;
+    } else {
+      split = j / a.splits;
+      piece = j % a.splits;
+    }
+    L = split_tile(a, split);
+    kt0 = piece * n_tiles / a.splits;
+    kt1 = (piece + 1) * n_tiles / a.splits;
   }
+  const int bh = L / a.q_tiles;
+  const int qt = L - bh * a.q_tiles;
+  const int q_row = qt * BM + wave * 32 + l32;
+  const bool q_ok = q_row < a.n_q;
 
   // Packed V with DV = 16: columns 16..31 of every V row stay zero in both buffers.
   if constexpr (!kNCHW && C::DVP > DV) {
@@ -281,9 +323,10 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     }
   }
 
-  // V residual: copy this tile's pixel columns of the V channels (NCHW only).
+  // V residual: copy this tile's pixel columns of the V channels (NCHW only;
+  // the first piece of a split tile does it).
   if constexpr (kNCHW) {
-    if (a.vres != nullptr) {
+    if (a.vres != nullptr && piece == 0) {
       const int n0 = qt * BM;
       constexpr int CPR = BM / 8;   // 8-pixel chunks per channel row
       for (int c = tid; c < DV * CPR; c += NT) {
@@ -302,68 +345,56 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   }
 
   // This lane's Q operands: Q[q_row][16*ds + 8*g + j], j = 0..7.
-  bf16x8 qop[kQB][NDS];
+  bf16x8 qop[NDS];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      u32x4 raw = zero4();
-      if (q_ok[qb]) {
-        if constexpr (kNCHW) {
-          const uint16_t* src = a.q + (static_cast<int64_t>(bh) * 4 * KD + ds * 16 + g * 8) * N + q_row[qb];
-          raw = gather8(src, N, 0, 8);
-        } else {
-          raw = load16(a.q + (static_cast<int64_t>(bh) * a.n_q + q_row[qb]) * KD + ds * 16 + g * 8);
-        }
+  for (int ds = 0; ds < NDS; ++ds) {
+    u32x4 raw = zero4();
+    if (q_ok) {
+      if constexpr (kNCHW) {
+        const uint16_t* src = a.q + (static_cast<int64_t>(bh) * 4 * KD + ds * 16 + g * 8) * N + q_row;
+        raw = gather8(src, N, 0, 8);
+      } else {
+        raw = load16(a.q + (static_cast<int64_t>(bh) * a.n_q + q_row) * KD + ds * 16 + g * 8);
       }
-      qop[qb][ds] = as_bf16x8(raw);
     }
-
-  f32x16 oacc[kQB][NDB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
-  float m_run[kQB], l_run[kQB];   // running max of scale*log2(e)*S; this lane's part of the sum
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.0f;
+    qop[ds] = as_bf16x8(raw);
   }
 
-  const int n_tiles = (a.n_k + kBN - 1) / kBN;
-  FwdStage<KD, DV, kNCHW, kVecN, kWaves, kQB> stage;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  float m_run = -INFINITY;   // running max of scale*log2(e)*S
+  float l_run = 0.0f;        // this lane's part of the running sum (its lane group's keys)
+
+  FwdStage<KD, DV, kNCHW, kVecN, kWaves> stage;
   FwdStageDirect<KD, DV, kWaves> dstage;
   if constexpr (kDirect) {
-    dstage.issue(a, bh, 0, wave, lane, smem);
+    dstage.issue(a, bh, kt0, wave, lane, smem + (kt0 & 1) * C::BUF);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
-    stage.load(a, bh, 0, tid);
-    stage.store(smem, tid);
+    stage.load(a, bh, kt0, tid);
+    stage.store(smem + (kt0 & 1) * C::BUF, tid);
   }
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     const uint16_t* ks = smem + (kt & 1) * C::BUF;
     const uint16_t* vs = ks + C::K_ELEMS;
-    const bool more = kt + 1 < n_tiles;
+    const bool more = kt + 1 < kt1;
     if constexpr (kDirect) {
       if (more) dstage.issue(a, bh, kt + 1, wave, lane, smem + ((kt + 1) & 1) * C::BUF);
     } else {
       if (more) stage.load(a, bh, kt + 1, tid);
     }
 
-    // S^T = K Q^T for the tile's keys (rows permuted by key_of_row); one K
-    // operand read serves every query block.
-    f32x16 sacc[kQB][NKB];
+    // S^T = K Q^T for the tile's keys (rows permuted by key_of_row).
+    f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         bf16x8 kop;
@@ -372,66 +403,56 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
                                  tr_key_col(i16 & 3), C::KROW);
         else
           kop = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + key_of_row(l32)) * C::KROW + ds * 16 + g * 8);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) sacc[qb][kb] = mfma32x32x16(kop, qop[qb][ds], sacc[qb][kb]);
+        sacc[kb] = mfma32x32x16(kop, qop[ds], sacc[kb]);
       }
     }
     // Keys past n_k (last tile only) get -inf. Element r of block kb holds
     // key 32*kb + 16*(r/8) + 8*g + r%8 of the tile.
     if ((kt + 1) * kBN > a.n_k) {
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt * kBN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-            if (key >= a.n_k) sacc[qb][kb][r] = -INFINITY;
-          }
-    }
-
-    // Online softmax per query block: running max, rescale, P = 2^(c*S - m).
-    bf16x8 pop[kQB][NKS];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float mx = sacc[qb][0][0];
-#pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
-      mx = fmaxf(mx, lane_xor32(mx, g));
-      const float m_tile = mx * a.c;
-#if PSA_LAZY_RESCALE
-      // The running max only moves when some lane's tile max exceeds it by
-      // more than 8 (log2 units): until then P <= 2^8, harmless in fp32 and bf16.
-      if (__any(m_tile > m_run[qb] + 8.0f)) {
-#else
-      {
-#endif
-        const float m_new = fmaxf(m_run[qb], m_tile);
-        const float alpha = fast_exp2(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-      }
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pop[qb][s][j] = static_cast<__bf16>(fast_exp2(fmaf(sacc[qb][s >> 1][8 * (s & 1) + j], a.c, -m_run[qb])));
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const bf16x2 pp = {pop[qb][s][j], pop[qb][s][j + 1]};
-          l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l_run[qb], false);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * kBN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+          if (key >= a.n_k) sacc[kb][r] = -INFINITY;
         }
+    }
+
+    // Online softmax: running max, rescale, P = 2^(c*S - m).
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, lane_xor32(mx, g));
+    const float m_tile = mx * a.c;
+    // The running max only moves when some lane's tile max exceeds it by more
+    // than 8 (log2 units): until then P <= 2^8, harmless in fp32 and bf16.
+    if (__any(m_tile > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+
+    bf16x8 pop[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        pop[s][j] = static_cast<__bf16>(fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -m_run)));
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const bf16x2 pp = {pop[s][j], pop[s][j + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l_run, false);
       }
     }
 
-    // O^T += V^T P^T: step s covers keys 16s + 8g + j of the tile in this lane's P;
-    // one V operand read serves every query block.
+    // O^T += V^T P^T: step s covers keys 16s + 8g + j of the tile in this lane's P.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -445,8 +466,7 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
         else
           vop = lds_read_tr8(vs + (s * 16 + 8 * g + (i16 >> 2)) * C::VROW + db * 32 + 16 * t16 + 4 * (i16 & 3),
                              C::VROW);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) oacc[qb][db] = mfma32x32x16(vop, pop[qb][s], oacc[qb][db]);
+        oacc[db] = mfma32x32x16(vop, pop[s], oacc[db]);
       }
 
     if constexpr (kDirect) {
@@ -457,32 +477,112 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     __syncthreads();
   }
 
-  // Epilogue: O = O^T / l, LSE = (m + log2 l) ln 2.
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float l_tot = l_run[qb] + lane_xor32(l_run[qb], g);
+  const float l_tot = l_run + lane_xor32(l_run, g);
+
+  if (split < 0) {
+    // Whole tile: O = O^T / l, LSE = (m + log2 l) ln 2.
     const float inv = 1.0f / l_tot;
-    if (!q_ok[qb]) continue;
+    if (!q_ok) return;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int dv0 = db * 32 + 8 * r4 + 4 * g;   // rows dv0 .. dv0+3 of this lane
+        const int dv0 = db * 32 + 8 * r4 + 4 * g;
         if (dv0 >= DV) continue;
         uint16_t h[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(oacc[qb][db][4 * r4 + e] * inv);
+        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(oacc[db][4 * r4 + e] * inv);
         if constexpr (kNCHW) {
-          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * DV + dv0) * N + q_row[qb];
+          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * DV + dv0) * N + q_row;
 #pragma unroll
           for (int e = 0; e < 4; ++e) dst[static_cast<int64_t>(e) * N] = h[e];
         } else {
-          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * a.n_q + q_row[qb]) * DV + dv0;
+          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * a.n_q + q_row) * DV + dv0;
           *reinterpret_cast<u32x2*>(dst) = u32x2{h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16)};
         }
       }
     if (a.lse != nullptr && g == 0)
-      a.lse[static_cast<int64_t>(bh) * a.n_q + q_row[qb]] = (m_run[qb] + log2f(l_tot)) * kLn2;
+      a.lse[static_cast<int64_t>(bh) * a.n_q + q_row] = (m_run + log2f(l_tot)) * kLn2;
+    return;
+  }
+
+  // Piece of a split tile: store unnormalised O^T, the running max and sum
+  // for the merge kernel.
+  {
+    float* pp = a.part + (static_cast<int64_t>(split) * a.splits + piece) * C::PART;
+    const int ql = wave * 32 + l32;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dv0 = db * 32 + 8 * r4 + 4 * g;
+        if (dv0 >= DV) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pp[(dv0 + e) * BM + ql] = oacc[db][4 * r4 + e];
+      }
+    if (g == 0) {
+      pp[DV * BM + ql] = m_run;
+      pp[DV * BM + BM + ql] = l_tot;
+    }
+  }
+}
+
+// Merge of split tiles. One workgroup per (split tile, 8 rows of O^T); each
+// thread owns 4 consecutive queries of one row. Per query, with M the largest
+// piece max m_c: w_c = 2^(m_c - M) / sum_c 2^(m_c - M) l_c, O = sum_c w_c O_c,
+// LSE = (M + log2 sum_c 2^(m_c - M) l_c) ln 2. Every load of a thread is
+// independent of the others, so the merge costs one or two memory round trips.
+constexpr int kMergeThreads = 256;
+
+template <int DV, bool kNCHW, int BM, int PART>
+__global__ __launch_bounds__(kMergeThreads) void attn_fwd_merge(FwdArgs a) {
+  constexpr int QV = BM / 4;                   // 4-query groups per row
+  constexpr int ROWS = kMergeThreads / QV;     // O^T rows per workgroup
+  constexpr int CHUNKS = DV / ROWS;
+  static_assert(kMergeThreads % QV == 0 && DV % ROWS == 0, "merge tiling");
+  const int split = blockIdx.x / CHUNKS;
+  const int dv = (blockIdx.x - split * CHUNKS) * ROWS + threadIdx.x / QV;
+  const int q4 = (threadIdx.x % QV) * 4;
+  const int L = split_tile(a, split);
+  const int bh = L / a.q_tiles;
+  const int qt = L - bh * a.q_tiles;
+  const int S = a.splits;
+  const float* part0 = a.part + static_cast<int64_t>(split) * S * PART;
+
+  f32x4 m[kMaxSplits], l[kMaxSplits], o[kMaxSplits];
+#pragma unroll
+  for (int c = 0; c < kMaxSplits; ++c) {
+    if (c < S) {
+      const float* pc = part0 + c * PART;
+      m[c] = *reinterpret_cast<const f32x4*>(pc + DV * BM + q4);
+      l[c] = *reinterpret_cast<const f32x4*>(pc + DV * BM + BM + q4);
+      o[c] = *reinterpret_cast<const f32x4*>(pc + dv * BM + q4);
+    } else {
+      m[c] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      l[c] = o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float M = m[0][e];
+#pragma unroll
+    for (int c = 1; c < kMaxSplits; ++c) M = fmaxf(M, m[c][e]);
+    float sum = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c) {
+      const float wc = fast_exp2(m[c][e] - M);   // 0 for pieces past S
+      sum = fmaf(wc, l[c][e], sum);
+      acc = fmaf(wc, o[c][e], acc);
+    }
+    const int row = qt * BM + q4 + e;
+    if (row >= a.n_q) continue;
+    const uint16_t h = float_to_bf16_bits(acc / sum);
+    if constexpr (kNCHW)
+      a.o[(static_cast<int64_t>(bh) * DV + dv) * a.n_k + row] = h;
+    else
+      a.o[(static_cast<int64_t>(bh) * a.n_q + row) * DV + dv] = h;
+    if (dv == 0 && a.lse != nullptr)
+      a.lse[static_cast<int64_t>(bh) * a.n_q + row] = (M + log2f(sum)) * kLn2;
   }
 }
 
@@ -576,28 +676,111 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
 
 // ------------------------------------------------------------------ dispatch
 
-#ifndef PSA_QB
-#define PSA_QB 1
-#endif
+// Compute units of the current device (0 if unknown).
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cus[dev] = n;
+  }
+  return cus[dev];
+}
 
-template <int KD, int DV, bool kNCHW, int kWaves>
-hipError_t run_bf16(FwdArgs a, bool vec_n, hipStream_t stream) {
-  // Two 32-query blocks per wave (one wave per SIMD) where the registers allow;
-  // head dim 128 keeps one block per wave.
-  constexpr int kQB = KD <= 64 ? PSA_QB : 1;
-  constexpr int BM = 32 * kQB * kWaves;
-#ifdef PSA_FWD_OCC
-  constexpr int kOcc = KD <= 64 ? PSA_FWD_OCC : 1;
-#else
-  constexpr int kOcc = (kQB == 1 && KD <= 64 && 2 * 2 * FwdCfg<KD, DV, kNCHW, kWaves, kQB>::BUF * 2 <= 160 * 1024) ? 2 : 1;
-#endif
-  a.q_tiles = (a.n_q + BM - 1) / BM;
-  const dim3 grid(static_cast<unsigned>(a.BH) * a.q_tiles);
-  if (vec_n)
-    attn_fwd_bf16<KD, DV, kNCHW, true, kWaves, kQB, kOcc><<<grid, kWaves * 64, 0, stream>>>(a);
-  else
-    attn_fwd_bf16<KD, DV, kNCHW, false, kWaves, kQB, kOcc><<<grid, kWaves * 64, 0, stream>>>(a);
+// Pieces per tail tile. With `slots` workgroups resident at once, `total`
+// query tiles leave rem = total mod slots for a last round. If that round
+// would fill at most half the slots, its tiles are cut into
+// min(slots / rem, n_tiles / kSplitMinTiles, kMaxSplits) key-range pieces,
+// when that is at least 2. Returns 1 (and rem = 0) for no split.
+int tail_splits(int total, int slots, int n_tiles, int& rem) {
+  rem = 0;
+  if (slots <= 0 || total <= slots) return 1;
+  const int r = total % slots;
+  if (r == 0 || 2 * r > slots) return 1;
+  int s = slots / r;
+  if (s > n_tiles / kSplitMinTiles) s = n_tiles / kSplitMinTiles;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 2) return 1;
+  rem = r;
+  return s;
+}
+
+// Query tiles, split plan and the workspace bytes the split needs for one
+// launch of attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc> on the current device.
+struct FwdPlan {
+  int q_tiles, full, tail, splits;
+  size_t bytes;
+};
+
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
+FwdPlan plan_bf16(int BH, int n_q, int n_k) {
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, kNCHW && kVecN>;
+  static int occ = -1;   // resident workgroups per CU (the same on every gfx950)
+  if (occ < 0) {
+    int n = 0;
+    occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &n, reinterpret_cast<const void*>(attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>),
+              C::NT, 0) == hipSuccess ? n : 0;
+  }
+  FwdPlan p;
+  p.q_tiles = (n_q + C::BM - 1) / C::BM;
+  const int total = BH * p.q_tiles;
+  int rem = 0;
+  p.splits = tail_splits(total, occ * cu_count(), (n_k + kBN - 1) / kBN, rem);
+  p.tail = rem;
+  p.full = total - rem;
+  p.bytes = sizeof(float) * static_cast<size_t>(C::PART) * rem * p.splits;
+  return p;
+}
+
+// Launches the forward; splits the tail only if `ws` holds the plan's bytes.
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
+hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, kNCHW && kVecN>;
+  FwdPlan p = plan_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>(a.BH, a.n_q, a.n_k);
+  if (p.tail > 0 && (ws == nullptr || ws_bytes < p.bytes)) {
+    p.full += p.tail;
+    p.tail = 0;
+    p.splits = 1;
+  }
+  a.q_tiles = p.q_tiles;
+  a.full = p.full;
+  a.tail = p.tail;
+  a.splits = p.splits;
+  a.part = static_cast<float*>(ws);
+  attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>
+      <<<dim3(static_cast<unsigned>(p.full + p.tail * p.splits)), C::NT, 0, stream>>>(a);
+  if (p.tail > 0) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    constexpr int chunks = DV / (kMergeThreads / (C::BM / 4));
+    attn_fwd_merge<DV, kNCHW, C::BM, C::PART>
+        <<<dim3(static_cast<unsigned>(p.tail * chunks)), kMergeThreads, 0, stream>>>(a);
+  }
   return hipGetLastError();
+}
+
+
+// Workgroups per CU the registers must allow for head dims up to 64: three
+// where the LDS also holds three (directly staged NCHW tiles, key_dim 64),
+// else two. Head dim 128 runs one.
+template <int KD, bool kNCHW, bool kVecN>
+constexpr int occ_target() {
+  return KD > 64 ? 1 : (kNCHW && kVecN && KD == 64) ? 3 : 2;
+}
+
+template <int KD, int DV, bool kNCHW>
+hipError_t run_bf16(FwdArgs a, bool vec_n, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (vec_n)
+    return launch_bf16<KD, DV, kNCHW, true, kWavesFwd, occ_target<KD, kNCHW, true>()>(a, ws, ws_bytes, stream);
+  return launch_bf16<KD, DV, kNCHW, false, kWavesFwd, occ_target<KD, kNCHW, false>()>(a, ws, ws_bytes, stream);
+}
+
+template <int KD, int DV, bool kNCHW>
+size_t split_bytes(int BH, int n_q, int n_k, bool vec_n) {
+  if (vec_n) return plan_bf16<KD, DV, kNCHW, true, kWavesFwd, occ_target<KD, kNCHW, true>()>(BH, n_q, n_k).bytes;
+  return plan_bf16<KD, DV, kNCHW, false, kWavesFwd, occ_target<KD, kNCHW, false>()>(BH, n_q, n_k).bytes;
 }
 
 template <int KD, bool kNCHW>
@@ -608,15 +791,34 @@ hipError_t run_f32(FwdArgsF32 a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifndef PSA_FWD_WAVES
-#define PSA_FWD_WAVES 4
-#endif
-constexpr int kWavesFwd = PSA_FWD_WAVES;
-
 }  // namespace
 
+size_t fa2_fwd_split_bytes(int BH, int n_q, int n_k, int D, bool bf16) {
+  if (!bf16) return 0;
+  switch (D) {
+    case 16: return split_bytes<16, 16, false>(BH, n_q, n_k, true);
+    case 32: return split_bytes<32, 32, false>(BH, n_q, n_k, true);
+    case 64: return split_bytes<64, 64, false>(BH, n_q, n_k, true);
+    case 128: return split_bytes<128, 128, false>(BH, n_q, n_k, true);
+  }
+  return 0;
+}
+
+size_t psa_fused_split_bytes(int BH, int KD, int N, bool bf16) {
+  if (!bf16) return 0;
+  const bool vec_n = (N % 8) == 0;
+  switch (KD) {
+    case 16: return split_bytes<16, 32, true>(BH, N, N, vec_n);
+    case 32: return split_bytes<32, 64, true>(BH, N, N, vec_n);
+    case 64: return split_bytes<64, 128, true>(BH, N, N, vec_n);
+    case 128: return split_bytes<128, 256, true>(BH, N, N, vec_n);
+  }
+  return 0;
+}
+
 hipError_t launch_fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                          int n_q, int n_k, int D, float scale, bool bf16, hipStream_t stream) {
+                          int n_q, int n_k, int D, float scale, bool bf16, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
   if (!bf16) {
     FwdArgsF32 a{static_cast<const float*>(q), static_cast<const float*>(k),
                  static_cast<const float*>(v), static_cast<float*>(o), nullptr, lse, BH, n_q, n_k,
@@ -629,20 +831,28 @@ hipError_t launch_fa2_fwd(const void* q, const void* k, const void* v, void* o, 
     }
     return hipErrorInvalidValue;
   }
-  FwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), nullptr, lse, BH, n_q, n_k,
-            0, scale * kLog2e};
+  FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.BH = BH;
+  a.n_q = n_q;
+  a.n_k = n_k;
+  a.c = scale * kLog2e;
   switch (D) {
-    case 16: return run_bf16<16, 16, false, kWavesFwd>(a, true, stream);
-    case 32: return run_bf16<32, 32, false, kWavesFwd>(a, true, stream);
-    case 64: return run_bf16<64, 64, false, kWavesFwd>(a, true, stream);
-    case 128: return run_bf16<128, 128, false, kWavesFwd>(a, true, stream);
+    case 16: return run_bf16<16, 16, false>(a, true, ws, ws_bytes, stream);
+    case 32: return run_bf16<32, 32, false>(a, true, ws, ws_bytes, stream);
+    case 64: return run_bf16<64, 64, false>(a, true, ws, ws_bytes, stream);
+    case 128: return run_bf16<128, 128, false>(a, true, ws, ws_bytes, stream);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_psa_fused_fwd(const void* qkv, void* out, void* vres, float* lse, int BH, int KD,
-                                int N, float scale, bool bf16, hipStream_t stream) {
+                                int N, float scale, bool bf16, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
   if (!bf16) {
     const float* x = static_cast<const float*>(qkv);
     FwdArgsF32 a{x, x, x, static_cast<float*>(out), static_cast<float*>(vres), lse, BH, N, N, scale};
@@ -655,14 +865,23 @@ hipError_t launch_psa_fused_fwd(const void* qkv, void* out, void* vres, float* l
     return hipErrorInvalidValue;
   }
   const uint16_t* x = static_cast<const uint16_t*>(qkv);
-  FwdArgs a{x, x, x, static_cast<uint16_t*>(out), static_cast<uint16_t*>(vres), lse, BH, N, N, 0,
-            scale * kLog2e};
+  FwdArgs a{};
+  a.q = x;
+  a.k = x;
+  a.v = x;
+  a.o = static_cast<uint16_t*>(out);
+  a.vres = static_cast<uint16_t*>(vres);
+  a.lse = lse;
+  a.BH = BH;
+  a.n_q = N;
+  a.n_k = N;
+  a.c = scale * kLog2e;
   const bool vec_n = (N % 8) == 0;
   switch (KD) {
-    case 16: return run_bf16<16, 32, true, kWavesFwd>(a, vec_n, stream);
-    case 32: return run_bf16<32, 64, true, kWavesFwd>(a, vec_n, stream);
-    case 64: return run_bf16<64, 128, true, kWavesFwd>(a, vec_n, stream);
-    case 128: return run_bf16<128, 256, true, kWavesFwd>(a, vec_n, stream);
+    case 16: return run_bf16<16, 32, true>(a, vec_n, ws, ws_bytes, stream);
+    case 32: return run_bf16<32, 64, true>(a, vec_n, ws, ws_bytes, stream);
+    case 64: return run_bf16<64, 128, true>(a, vec_n, ws, ws_bytes, stream);
+    case 128: return run_bf16<128, 256, true>(a, vec_n, ws, ws_bytes, stream);
   }
   return hipErrorInvalidValue;
 }

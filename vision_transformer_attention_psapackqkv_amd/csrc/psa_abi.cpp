@@ -163,29 +163,39 @@ psa_status psa_merge_attn(const void* o2, void* out_nchw, int B, int heads, int 
                                                elt_bytes(dtype), as_stream(stream)));
 }
 
+size_t fa2_fwd_workspace_bytes(int BH, int n_q, int n_k, int head_dim, psa_dtype dtype) {
+  if (BH <= 0 || n_q <= 0 || n_k <= 0 || !supported_dim(head_dim) ||
+      (dtype != PSA_F32 && dtype != PSA_BF16))
+    return 0;
+  return psa::fa2_fwd_split_bytes(BH, n_q, n_k, head_dim, dtype == PSA_BF16);
+}
+
 psa_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                   int n_q, int n_k, int head_dim, float scale, psa_dtype dtype, void* stream) {
+                   int n_q, int n_k, int head_dim, float scale, psa_dtype dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   const char* fn = "fa2_fwd";
   if (!q || !k || !v || !o)
-    return fail(PSA_ERR_NULL, fn, "q, k, v and o must not be NULL (lse may be)");
+    return fail(PSA_ERR_NULL, fn, "q, k, v and o must not be NULL (lse and workspace may be)");
   PSA_TRY(check_attn(fn, BH, n_q, n_k, head_dim, scale, dtype));
-  const char* names[5] = {"q", "k", "v", "o", "lse"};
-  const void* ptrs[5] = {q, k, v, o, lse};
-  for (int i = 0; i < 5; ++i)
+  const char* names[6] = {"q", "k", "v", "o", "lse", "workspace"};
+  const void* ptrs[6] = {q, k, v, o, lse, workspace};
+  for (int i = 0; i < 6; ++i)
     if (ptrs[i]) PSA_TRY(check_aligned(fn, names[i], ptrs[i]));
   const int64_t eb = elt_bytes(dtype);
   const int64_t nq = static_cast<int64_t>(BH) * n_q * head_dim;
   const int64_t nk = static_cast<int64_t>(BH) * n_k * head_dim;
-  const Range outs[2] = {range("o", o, nq, eb), range("lse", lse, static_cast<int64_t>(BH) * n_q, 4)};
+  const Range outs[3] = {range("o", o, nq, eb), range("lse", lse, static_cast<int64_t>(BH) * n_q, 4),
+                         range("workspace", workspace, workspace ? static_cast<int64_t>(workspace_bytes) : 0, 1)};
   const Range ins[3] = {range("q", q, nq, eb), range("k", k, nk, eb), range("v", v, nk, eb)};
   for (const Range& a : outs)
     for (const Range& b : ins) {
       const Range pair[2] = {a, b};
       PSA_TRY(check_disjoint(fn, pair, 2));
     }
-  PSA_TRY(check_disjoint(fn, outs, 2));
+  PSA_TRY(check_disjoint(fn, outs, 3));
   return launched(fn, psa::launch_fa2_fwd(q, k, v, o, lse, BH, n_q, n_k, head_dim, scale,
-                                          dtype == PSA_BF16, as_stream(stream)));
+                                          dtype == PSA_BF16, workspace,
+                                          workspace ? workspace_bytes : 0, as_stream(stream)));
 }
 
 size_t fa2_bwd_workspace_bytes(int BH, int n_q) {
@@ -223,9 +233,21 @@ psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
                                           as_stream(stream)));
 }
 
+size_t psa_attention_fwd_workspace_bytes(int B, int heads, int key_dim, int H, int W,
+                                         psa_dtype dtype) {
+  if (B <= 0 || heads <= 0 || H <= 0 || W <= 0 || !supported_dim(key_dim) ||
+      (dtype != PSA_F32 && dtype != PSA_BF16))
+    return 0;
+  const int64_t N = static_cast<int64_t>(H) * W;
+  const int64_t BH = static_cast<int64_t>(B) * heads;
+  if (N > (1 << 28) || BH > (1 << 24)) return 0;
+  return psa::psa_fused_split_bytes(static_cast<int>(BH), key_dim, static_cast<int>(N),
+                                    dtype == PSA_BF16);
+}
+
 psa_status psa_attention_fwd(const void* qkv_nchw, void* out_nchw, void* v_nchw, float* lse, int B,
                              int heads, int key_dim, int H, int W, float scale, psa_dtype dtype,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "psa_attention_fwd";
   if (!qkv_nchw) return fail(PSA_ERR_NULL, fn, "qkv_nchw is NULL");
   if (!out_nchw) return fail(PSA_ERR_NULL, fn, "out_nchw is NULL");
@@ -236,15 +258,18 @@ psa_status psa_attention_fwd(const void* qkv_nchw, void* out_nchw, void* v_nchw,
   PSA_TRY(check_aligned(fn, "out_nchw", out_nchw));
   if (v_nchw) PSA_TRY(check_aligned(fn, "v_nchw", v_nchw));
   if (lse) PSA_TRY(check_aligned(fn, "lse", lse));
+  if (workspace) PSA_TRY(check_aligned(fn, "workspace", workspace));
   const int64_t eb = elt_bytes(dtype);
   const int64_t half = static_cast<int64_t>(B) * heads * key_dim * H * W;  // elements per [., KD] set
-  const Range r[4] = {range("qkv_nchw", qkv_nchw, 4 * half, eb),
+  const Range r[5] = {range("qkv_nchw", qkv_nchw, 4 * half, eb),
                       range("out_nchw", out_nchw, 2 * half, eb),
                       range("v_nchw", v_nchw, v_nchw ? 2 * half : 0, eb),
-                      range("lse", lse, lse ? static_cast<int64_t>(B) * heads * H * W : 0, 4)};
-  PSA_TRY(check_disjoint(fn, r, 4));
+                      range("lse", lse, lse ? static_cast<int64_t>(B) * heads * H * W : 0, 4),
+                      range("workspace", workspace, workspace ? static_cast<int64_t>(workspace_bytes) : 0, 1)};
+  PSA_TRY(check_disjoint(fn, r, 5));
   return launched(fn, psa::launch_psa_fused_fwd(qkv_nchw, out_nchw, v_nchw, lse, B * heads,
-                                                key_dim, H * W, scale, dtype == PSA_BF16,
+                                                key_dim, H * W, scale, dtype == PSA_BF16, workspace,
+                                                workspace ? workspace_bytes : 0,
                                                 as_stream(stream)));
 }
 

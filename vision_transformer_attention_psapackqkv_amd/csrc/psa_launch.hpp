@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace psa {
@@ -17,13 +18,18 @@ hipError_t launch_pack_qkv(const void* qkv, void* packed, int BH, int KD, int N,
 hipError_t launch_rows_to_nchw(const void* rows, void* nchw, int BH, int KD, int N, int slot0,
                                int elt_bytes, hipStream_t stream);
 
-// FA2 forward on [BH, n, D] tensors.
+// FA2 forward on [BH, n, D] tensors. ws / ws_bytes: workspace for the tail
+// split (used only if it holds fa2_fwd_split_bytes; may be null).
 hipError_t launch_fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                          int n_q, int n_k, int D, float scale, bool bf16, hipStream_t stream);
+                          int n_q, int n_k, int D, float scale, bool bf16, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+size_t fa2_fwd_split_bytes(int BH, int n_q, int n_k, int D, bool bf16);
 
 // Fused PSA forward: qkv [B, 4hKD, H, W] -> out [B, 2hKD, H, W] (+ V residual, + LSE).
 hipError_t launch_psa_fused_fwd(const void* qkv, void* out, void* vres, float* lse, int BH, int KD,
-                                int N, float scale, bool bf16, hipStream_t stream);
+                                int N, float scale, bool bf16, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+size_t psa_fused_split_bytes(int BH, int KD, int N, bool bf16);
 
 // FA2 backward: Delta into workspace, then the dK/dV and dQ kernels.
 hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const void* o,
