@@ -6,5 +6,8 @@ from .psa_oracle import (  # noqa: F401
     extract_v,
     merge_attn,
     pack_qkv,
+    psa_backward,
     psa_forward,
+    split_attn,
+    unpack_qkv,
 )

@@ -106,6 +106,45 @@ def merge_attn(o2: np.ndarray, B: int, heads: int, key_dim: int, H: int, W: int)
     return out.reshape(B, C, H, W)
 
 
+def split_attn(out: np.ndarray, B: int, heads: int, key_dim: int, H: int, W: int) -> np.ndarray:
+    """Inverse (and adjoint) of :func:`merge_attn`:
+    ``o2[j, b*heads+i, n, d] = out[b, i*2*KD + j*KD + d, y, x]``.
+
+    The merge is a permutation, so the gradient reaching its NCHW output goes
+    back to the two ``[BH, N, KD]`` halves by the inverse permutation
+    (vision-rs book, "Custom Kernels", "Position-Sensitive Attention (PSA)",
+    PsaMergeAttn bullet, read backwards).
+    """
+    KD, N, BH, C = key_dim, H * W, B * heads, 2 * heads * key_dim
+    flat = np.asarray(out).reshape(-1)
+    assert flat.size == B * C * N, "out has the wrong number of elements"
+    bh, n, d = np.ix_(np.arange(BH), np.arange(N), np.arange(KD))
+    b, i = bh // heads, bh % heads
+    o2 = np.empty((2, BH, N, KD), dtype=flat.dtype)
+    for j in range(2):
+        o2[j] = flat[_nchw_flat(b, i * 2 * KD + j * KD + d, n, C, N)]
+    return o2
+
+
+def unpack_qkv(packed: np.ndarray, B: int, heads: int, key_dim: int, H: int, W: int) -> np.ndarray:
+    """Inverse (and adjoint) of :func:`pack_qkv`:
+    ``qkv[b, i*4*KD + s*KD + d, y, x] = packed[s, b*heads+i, n, d]``.
+
+    The pack is a permutation, so gradients with respect to the packed Q, K,
+    V_lo, V_hi reach the NCHW QKV tensor by the inverse permutation (vision-rs
+    book, "Custom Kernels", "Position-Sensitive Attention (PSA)", PsaPackQkv
+    bullet, read backwards).
+    """
+    KD, N, BH, C = key_dim, H * W, B * heads, 4 * heads * key_dim
+    packed = np.asarray(packed).reshape(4, BH, N, KD)
+    out = np.empty(B * C * N, dtype=packed.dtype)
+    bh, n, d = np.ix_(np.arange(BH), np.arange(N), np.arange(KD))
+    b, i = bh // heads, bh % heads
+    for s in range(4):
+        out[_nchw_flat(b, i * 4 * KD + s * KD + d, n, C, N)] = packed[s]
+    return out.reshape(B, C, H, W)
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     """softmax(scale * Q K^T) V and the row log-sum-exp, per batch-head, in float64.
 
@@ -176,3 +215,39 @@ def psa_forward(qkv: np.ndarray, B: int, heads: int, key_dim: int, H: int, W: in
     out = merge_attn(np.stack([o_lo, o_hi]), B, heads, key_dim, H, W)
     v_res = extract_v(packed, B, heads, key_dim, H, W)
     return out, v_res, lse
+
+
+def psa_backward(qkv: np.ndarray, dout: np.ndarray, dv_res, B: int, heads: int, key_dim: int,
+                 H: int, W: int, scale: float | None = None) -> np.ndarray:
+    """Gradient of the PSA forward with respect to the NCHW QKV tensor, in float64.
+
+    The forward (vision-rs book, "Custom Kernels", "Position-Sensitive
+    Attention (PSA)") is pack -> FA2 on (Q, K, V_lo) and on (Q, K, V_hi) ->
+    merge, plus extract V for the residual path. Its gradient is the chain
+    rule through those steps, taken in reverse:
+
+    * ``dout`` (gradient of ``out``, NCHW ``[B, 2hKD, H, W]``) goes back through
+      the merge permutation to the two halves (:func:`split_attn`);
+    * each half's FA2 backward (:func:`attention_bwd`, "Flash Attention 2")
+      gives dQ_j, dK_j, dV_j; Q and K are shared by both halves, so their
+      gradients are the sums dQ_lo + dQ_hi and dK_lo + dK_hi;
+    * ``dv_res`` (gradient of the V residual output, NCHW ``[B, 2hKD, H, W]``,
+      or None for zero) goes back through the extract permutation and adds to
+      dV_lo, dV_hi;
+    * the four packed gradients go back through the pack permutation
+      (:func:`unpack_qkv`).
+
+    Readings: no gradient flows through the LSE (it is saved state, not an
+    output of the block); the scale is KEY_DIM ** -0.5 unless given.
+    """
+    if scale is None:
+        scale = default_scale(key_dim)
+    x = np.asarray(qkv, dtype=np.float64)
+    packed = pack_qkv(x, B, heads, key_dim, H, W)
+    do2 = split_attn(np.asarray(dout, dtype=np.float64), B, heads, key_dim, H, W)
+    dq_lo, dk_lo, dv_lo = attention_bwd(packed[0], packed[1], packed[2], do2[0], scale)
+    dq_hi, dk_hi, dv_hi = attention_bwd(packed[0], packed[1], packed[3], do2[1], scale)
+    dpacked = np.stack([dq_lo + dq_hi, dk_lo + dk_hi, dv_lo, dv_hi])
+    if dv_res is not None:
+        dpacked[2:] += split_attn(np.asarray(dv_res, dtype=np.float64), B, heads, key_dim, H, W)
+    return unpack_qkv(dpacked, B, heads, key_dim, H, W)

@@ -208,3 +208,68 @@ def check_attention_bwd(attention_bwd, attention):
     # Q = 0: every P entry is 1/N_k, so dV[m] = (1/N_k) sum_n dO[n] for every key m
     _, _, dv0 = attention_bwd(np.zeros_like(q), k, v, g, 0.5)
     assert np.allclose(dv0, np.repeat(g.sum(axis=1, keepdims=True) / 9.0, 9, axis=1), atol=1e-12), "Q=0: dV"
+
+
+# --------------------------------------------------------------------- PSA backward
+
+def _psa_torch(x, B, h, KD, H, W, s):
+    """The PSA forward written with torch reshapes (a route independent of the oracle):
+    channels split as (head, slot, d), the map flattened row-major."""
+    t = x.reshape(B, h, 4, KD, H * W)
+    q = t[:, :, 0].transpose(-1, -2)
+    k = t[:, :, 1].transpose(-1, -2)
+    v = torch.cat([t[:, :, 2], t[:, :, 3]], dim=2).transpose(-1, -2)      # [B, h, N, 2KD]
+    p = torch.softmax(s * q @ k.transpose(-1, -2), dim=-1)
+    out = (p @ v).transpose(-1, -2).reshape(B, 2 * h * KD, H, W)
+    vres = t[:, :, 2:4].reshape(B, 2 * h * KD, H, W)
+    return out, vres
+
+
+def check_psa_backward(psa_backward, psa_forward):
+    rng = _rng(11)
+    # 1) central finite differences of L = <dout, out> + <dvres, v_res> through the forward
+    B, h, KD, H, W = 1, 2, 2, 2, 2
+    s = 0.7
+    x = rng.normal(size=(B, 4 * h * KD, H, W))
+    g = rng.normal(size=(B, 2 * h * KD, H, W))
+    gv = rng.normal(size=(B, 2 * h * KD, H, W))
+
+    def loss(xx):
+        out, vres, _ = psa_forward(xx, B, h, KD, H, W, s)
+        return float((out * g).sum() + (vres * gv).sum())
+
+    dx = psa_backward(x, g, gv, B, h, KD, H, W, s)
+    assert dx.shape == x.shape, "d(qkv) has the wrong shape"
+    eps = 1e-6
+    num = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        old = x[idx]
+        x[idx] = old + eps; lp = loss(x)
+        x[idx] = old - eps; lm = loss(x)
+        x[idx] = old
+        num[idx] = (lp - lm) / (2 * eps)
+    assert np.allclose(dx, num, atol=1e-8, rtol=1e-6), "PSA backward disagrees with finite differences"
+    # 2) torch float64 autograd through the torch-written forward, larger shapes
+    B, h, KD, H, W = 2, 3, 4, 3, 5
+    s = KD ** -0.5
+    x = rng.normal(size=(B, 4 * h * KD, H, W))
+    g = rng.normal(size=(B, 2 * h * KD, H, W))
+    gv = rng.normal(size=(B, 2 * h * KD, H, W))
+    tx = torch.tensor(x, requires_grad=True)
+    out, vres = _psa_torch(tx, B, h, KD, H, W, s)
+    ((out * torch.tensor(g)).sum() + (vres * torch.tensor(gv)).sum()).backward()
+    dx = psa_backward(x, g, gv, B, h, KD, H, W, s)
+    assert np.allclose(dx, tx.grad.numpy(), atol=1e-11, rtol=0), "PSA backward disagrees with torch autograd"
+    # without the residual gradient (None) it equals the gradient of <dout, out> alone
+    tx.grad = None
+    out, _ = _psa_torch(tx, B, h, KD, H, W, s)
+    (out * torch.tensor(g)).sum().backward()
+    dx0 = psa_backward(x, g, None, B, h, KD, H, W, None)
+    assert np.allclose(dx0, tx.grad.numpy(), atol=1e-11, rtol=0), "PSA backward without dv_res"
+    # 3) invariants per head: K channels' gradient sums to 0 over the map (K -> K + u leaves
+    #    the output unchanged); V channels' gradient sums to the map-sum of dout (+ dv_res),
+    #    since the rows of P sum to 1
+    dxr = dx.reshape(B, h, 4, KD, H * W)
+    assert np.allclose(dxr[:, :, 1].sum(axis=-1), 0.0, atol=1e-11), "sum over pixels of dK != 0"
+    gr = (g + gv).reshape(B, h, 2, KD, H * W).sum(axis=-1)
+    assert np.allclose(dxr[:, :, 2:4].sum(axis=-1), gr, atol=1e-11), "sum over pixels of dV"

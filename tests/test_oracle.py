@@ -155,3 +155,44 @@ def test_golden_catches_section_major_pack():
                 O.extract_v(packed, B, heads, key_dim, H, W), lse)
     with pytest.raises(AssertionError):
         pins.check_psa_golden(psa_forward, _pack_variant("section_major"))
+
+
+def test_psa_backward_pins():
+    pins.check_psa_backward(O.psa_backward, O.psa_forward)
+
+
+def test_layout_inverses():
+    """split_attn undoes merge_attn and unpack_qkv undoes pack_qkv (the adjoints of
+    permutations are their inverses), also on raw bits."""
+    B, h, KD, H, W = 2, 3, 4, 3, 5
+    rng = np.random.default_rng(3)
+    x = rng.integers(0, 2**16, size=(B, 4 * h * KD, H, W)).astype(np.uint16)
+    assert np.array_equal(O.unpack_qkv(O.pack_qkv(x, B, h, KD, H, W), B, h, KD, H, W), x)
+    o = rng.integers(0, 2**16, size=(B, 2 * h * KD, H, W)).astype(np.uint16)
+    assert np.array_equal(O.merge_attn(O.split_attn(o, B, h, KD, H, W), B, h, KD, H, W), o)
+    o2 = rng.integers(0, 2**16, size=(2, B * h, H * W, KD)).astype(np.uint16)
+    assert np.array_equal(O.split_attn(O.merge_attn(o2, B, h, KD, H, W), B, h, KD, H, W), o2)
+
+
+def _psa_bwd_variant(mode):
+    def psa_backward(qkv, dout, dv_res, B, heads, key_dim, H, W, scale=None):
+        s = O.default_scale(key_dim) if scale is None else scale
+        packed = O.pack_qkv(np.asarray(qkv, dtype=np.float64), B, heads, key_dim, H, W)
+        do2 = O.split_attn(np.asarray(dout, dtype=np.float64), B, heads, key_dim, H, W)
+        if mode == "halves_swapped":
+            do2 = do2[::-1]
+        dq0, dk0, dv0 = O.attention_bwd(packed[0], packed[1], packed[2], do2[0], s)
+        dq1, dk1, dv1 = O.attention_bwd(packed[0], packed[1], packed[3], do2[1], s)
+        dq = dq0 if mode == "dq_lo_only" else dq0 + dq1
+        dk = dk1 if mode == "dk_hi_only" else dk0 + dk1
+        dp = np.stack([dq, dk, dv0, dv1])
+        if dv_res is not None and mode != "no_vres":
+            dp[2:] += O.split_attn(np.asarray(dv_res, dtype=np.float64), B, heads, key_dim, H, W)
+        return O.unpack_qkv(dp, B, heads, key_dim, H, W)
+    return psa_backward
+
+
+@pytest.mark.parametrize("mode", ["halves_swapped", "dq_lo_only", "dk_hi_only", "no_vres"])
+def test_psa_backward_mutants_are_caught(mode):
+    with pytest.raises(AssertionError):
+        pins.check_psa_backward(_psa_bwd_variant(mode), O.psa_forward)
