@@ -166,6 +166,34 @@ psa_status psa_attention_fwd(const void* qkv_nchw, void* out_nchw, void* v_nchw,
 size_t psa_attention_fwd_workspace_bytes(int B, int heads, int key_dim, int H, int W,
                                          psa_dtype dtype);
 
+/*
+ * PSA backward: the gradient of psa_attention_fwd's outputs with respect to
+ * qkv_nchw, i.e. the forward's steps (PsaPackQkv, FA2 over (Q, K, V_lo) and
+ * (Q, K, V_hi), PsaMergeAttn, PsaExtractV; vision-rs book, "Custom Kernels",
+ * "Position-Sensitive Attention (PSA)" and "Flash Attention 2") taken in
+ * reverse. With P = exp(scale*Q K^T - lse), dO = the two halves of dout_nchw,
+ * O = the two halves of out_nchw, V = [V_lo | V_hi], Delta = rowsum(dO * O):
+ *   dS = P * (dO V^T - Delta)
+ *   dqkv[Q]  = scale * dS K        (the sum of both halves' dQ)
+ *   dqkv[K]  = scale * dS^T Q      (the sum of both halves' dK)
+ *   dqkv[V]  = P^T dO + dv_nchw    (per half; the V residual's gradient adds)
+ * written in the NCHW channel order of qkv_nchw. No gradient flows through lse.
+ * qkv_nchw: [B, 4*h*KD, H, W] forward input. out_nchw, lse: the forward's
+ * output [B, 2*h*KD, H, W] and LSE [B*h, H*W] (as psa_attention_fwd wrote them).
+ * dout_nchw: [B, 2*h*KD, H, W] gradient of out. dv_nchw: [B, 2*h*KD, H, W]
+ * gradient of the V residual, or NULL for none. dqkv_nchw: [B, 4*h*KD, H, W]
+ * output. workspace: caller-owned float32 scratch of
+ * psa_attention_bwd_workspace_bytes(B, heads, H, W) bytes. PSA_BF16 only
+ * (PSA_F32 returns PSA_ERR_UNSUPPORTED). scale: the forward's.
+ */
+psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const float* lse,
+                             const void* dout_nchw, const void* dv_nchw, void* dqkv_nchw,
+                             float* workspace, int B, int heads, int key_dim, int H, int W,
+                             float scale, psa_dtype dtype, void* stream);
+
+/* Bytes of workspace psa_attention_bwd needs: 2 * B*h * H*W floats. 0 if a size is invalid. */
+size_t psa_attention_bwd_workspace_bytes(int B, int heads, int H, int W);
+
 /* Message of the last error on this thread ("" after a success). */
 const char* psa_last_error(void);
 

@@ -156,3 +156,36 @@ def test_error_string_cleared_on_next_error_free_path():
     # workspace-size query does not touch the error state; a later error overwrites it
     lib.psa_merge_attn(A, None, 1, 1, 16, 1, 1, 1, None)
     assert lib.psa_last_error().decode().startswith("psa_merge_attn")
+
+
+def test_psa_attention_bwd_argument_errors():
+    lib = psa.load_library()
+    assert lib.psa_attention_bwd_workspace_bytes(32, 8, 40, 40) == 2 * 256 * 1600 * 4
+    assert lib.psa_attention_bwd_workspace_bytes(0, 8, 40, 40) == 0
+    base = [0x1000000 * (i + 1) for i in range(7)]   # qkv, out, lse, dout, dv, dqkv, workspace
+
+    def call(ptrs=base, B=1, h=2, kd=32, H=4, W=4, s=0.2, dt=1):
+        return _status("psa_attention_bwd", *ptrs, B, h, kd, H, W, ctypes.c_float(s), dt, None)
+
+    for i in (0, 1, 2, 3, 5, 6):
+        p = list(base)
+        p[i] = None
+        st, msg = call(p)
+        assert st == 1 and msg.startswith("psa_attention_bwd"), (i, st, msg)
+    p = list(base)
+    p[4] = None                       # no residual gradient: valid, so the failure is elsewhere
+    assert call(p, kd=24)[0] == 3
+    assert call(kd=48)[0] == 3
+    st, msg = call(dt=0)
+    assert st == 3 and "PSA_BF16" in msg
+    assert call(H=0)[0] == 2
+    assert call(s=float("nan"))[0] == 3
+    p = list(base)
+    p[3] = base[3] + 2
+    assert call(p)[0] == 4
+    p = list(base)
+    p[5] = base[0]                    # dqkv aliases qkv
+    assert call(p)[0] == 5
+    p = list(base)
+    p[6] = base[5] + 64               # workspace inside dqkv
+    assert call(p)[0] == 5

@@ -1,0 +1,121 @@
+"""The PSA backward (psa_attention_bwd: d(qkv) NCHW from dOut and the V-residual gradient)
+on the GPU against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import psa_inputs as I
+import vision_transformer_attention_psapackqkv_amd as psa
+from oracle import psa_oracle as O
+from tests.gpu_helpers import announce, assert_attention_close, device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+# (B, heads, key_dim, H, W): several key and query tiles with ragged tails, every key_dim,
+# N a multiple of 8 (tiles staged straight into LDS) and not (staged through registers).
+SHAPES = [
+    (1, 2, 16, 8, 8),       # N = 64, one tile
+    (2, 2, 32, 16, 16),     # N = 256, whole tiles
+    (2, 1, 32, 7, 9),       # N = 63
+    (1, 2, 64, 10, 13),     # N = 130
+    (1, 2, 64, 12, 12),     # N = 144
+    (1, 1, 128, 9, 12),     # N = 108
+    (1, 1, 16, 1, 1),       # one pixel
+    (3, 2, 32, 20, 20),     # N = 400
+]
+
+
+def _id(s):
+    return "B{}h{}kd{}_{}x{}".format(*s)
+
+
+def _inputs(B, h, KD, H, W, seed, with_dv):
+    qkv = I.make_qkv(B, h, KD, H, W, seed=seed)
+    g = torch.from_numpy(np.random.default_rng(seed + 1).standard_normal((B, 2 * h * KD, H, W)).astype(np.float32))
+    dout = g.to(torch.bfloat16)
+    dv = None
+    if with_dv:
+        gv = np.random.default_rng(seed + 2).standard_normal((B, 2 * h * KD, H, W)).astype(np.float32)
+        dv = torch.from_numpy(gv).to(torch.bfloat16)
+    return qkv, dout, dv
+
+
+def _run(qkv, dout, dv, h, KD, dev):
+    x = qkv.to(dev)
+    out, _, lse = psa.psa_attention_fwd(x, h, KD, want_v=False)
+    return psa.psa_attention_bwd(x, out, lse, dout.to(dev), h, KD, dv=None if dv is None else dv.to(dev))
+
+
+@pytest.mark.parametrize("with_dv", [False, True], ids=["no_dv", "dv"])
+@pytest.mark.parametrize("shape", SHAPES, ids=_id)
+def test_psa_attention_bwd(shape, with_dv):
+    dev = device()
+    B, h, KD, H, W = shape
+    announce(f"psa_attention_bwd {_id(shape)} dv={with_dv}")
+    qkv, dout, dv = _inputs(B, h, KD, H, W, 17 * B + h + KD + H * W, with_dv)
+    got = _run(qkv, dout, dv, h, KD, dev)
+    want = O.psa_backward(to_f64(qkv), to_f64(dout), None if dv is None else to_f64(dv), B, h, KD, H, W)
+    g = to_f64(got).reshape(B, h, 4, KD, H * W)
+    wr = want.reshape(B, h, 4, KD, H * W)
+    for s, name in enumerate(("dQ", "dK", "dV_lo", "dV_hi")):
+        assert_attention_close(g[:, :, s], wr[:, :, s], "bf16", f"psa_attention_bwd {name}")
+
+
+def test_psa_attention_bwd_40x40():
+    """The 40x40 map at full size (B=32, heads=8, key_dim=32: BH=256, N=1600), through the
+    launch configuration bench.py times; batch items 0 and 31 (16 heads) against the oracle,
+    and on every head the invariant that each K channel's gradient sums to 0 over the map."""
+    dev = device()
+    B, h, KD, H, W = 32, 8, 32, 40, 40
+    announce("psa_attention_bwd 40x40 full size")
+    qkv, dout, dv = _inputs(B, h, KD, H, W, 2024, True)
+    got = _run(qkv, dout, dv, h, KD, dev)
+    g = to_f64(got)
+    for b in (0, B - 1):
+        want = O.psa_backward(to_f64(qkv[b:b + 1]), to_f64(dout[b:b + 1]), to_f64(dv[b:b + 1]), 1, h, KD, H, W)
+        gb = g[b:b + 1].reshape(1, h, 4, KD, H * W)
+        wb = want.reshape(1, h, 4, KD, H * W)
+        for s, name in enumerate(("dQ", "dK", "dV_lo", "dV_hi")):
+            assert_attention_close(gb[:, :, s], wb[:, :, s], "bf16", f"40x40 b={b} {name}")
+    ksum = g.reshape(B, h, 4, KD, H * W)[:, :, 1].sum(axis=-1)
+    scale = np.abs(g.reshape(B, h, 4, KD, H * W)[:, :, 1]).sum(axis=-1).max()
+    assert np.abs(ksum).max() <= 1e-2 * scale, "sum over pixels of dK is not ~0"
+
+
+def test_psa_attention_bwd_matches_two_fa2_bwd():
+    """The fused backward equals the unfused composition built from the library's own calls
+    (pack, fa2_bwd per V half, dQ and dK summed) to within bf16 rounding."""
+    dev = device()
+    B, h, KD, H, W = 2, 2, 32, 12, 12
+    announce("psa_attention_bwd vs two fa2_bwd")
+    qkv, dout, _ = _inputs(B, h, KD, H, W, 99, False)
+    x = qkv.to(dev)
+    out, _, lse = psa.psa_attention_fwd(x, h, KD, want_v=False)
+    fused = to_f64(psa.psa_attention_bwd(x, out, lse, dout.to(dev), h, KD)).reshape(B, h, 4, KD, H * W)
+    N = H * W
+
+    def halves(t):   # NCHW [B, 2hKD, H, W] -> the (lo, hi) halves as contiguous [BH, N, KD]
+        r = t.reshape(B, h, 2, KD, N)
+        return [r[:, :, j].permute(0, 1, 3, 2).reshape(B * h, N, KD).contiguous() for j in range(2)]
+
+    packed = psa.psa_pack_qkv(x, h, KD)
+    o_lo, o_hi = halves(out)
+    g_lo, g_hi = halves(dout.to(dev))
+    lo = psa.fa2_bwd(packed[0], packed[1], packed[2], o_lo, g_lo, lse)
+    hi = psa.fa2_bwd(packed[0], packed[1], packed[3], o_hi, g_hi, lse)
+
+    def nchw(t):   # [BH, N, KD] -> [B, h, KD, N]
+        return to_f64(t).reshape(B, h, N, KD).transpose(0, 1, 3, 2)
+    ref = [nchw(lo[0]) + nchw(hi[0]), nchw(lo[1]) + nchw(hi[1]), nchw(lo[2]), nchw(hi[2])]
+    for s, name in enumerate(("dQ", "dK", "dV_lo", "dV_hi")):
+        assert_attention_close(fused[:, :, s], ref[s], "bf16", f"fused vs composed {name}")
+
+
+def test_psa_attention_bwd_repeatable():
+    dev = device()
+    B, h, KD, H, W = 1, 2, 64, 16, 16
+    announce("psa_attention_bwd repeatable")
+    qkv, dout, dv = _inputs(B, h, KD, H, W, 5, True)
+    a = _run(qkv, dout, dv, h, KD, dev)
+    b = _run(qkv, dout, dv, h, KD, dev)
+    assert torch.equal(a, b)

@@ -31,6 +31,8 @@ SIGNATURES = {
     "fa2_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "psa_attention_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]),
     "psa_attention_fwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
+    "psa_attention_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "psa_attention_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "psa_last_error": (ctypes.c_char_p, []),
     "psa_abi_version": (_I, []),
 }
@@ -220,6 +222,32 @@ def psa_attention_fwd(qkv, heads, key_dim, scale=None, want_v=True, want_lse=Tru
     _check(lib.psa_attention_fwd(qkv.data_ptr(), _dev(out, "out").data_ptr(), _ptr(v_out),
                                  _ptr(lse), B, heads, key_dim, H, W, s, code, wp, wb, _stream(qkv)))
     return out, v_out, lse
+
+
+def psa_attention_bwd(qkv, out, lse, dout, heads, key_dim, dv=None, scale=None, dqkv=None,
+                      workspace=None):
+    """PSA backward: the gradient of ``psa_attention_fwd``'s outputs with respect to ``qkv``.
+
+    ``out`` and ``lse`` are the forward's, ``dout`` the gradient of ``out``, ``dv`` the gradient
+    of the V residual (None: none). Returns ``dqkv`` NCHW ``[B, 4*heads*key_dim, H, W]``."""
+    for t, n in ((qkv, "qkv"), (out, "out"), (lse, "lse"), (dout, "dout")):
+        _dev(t, n)
+    if dv is not None:
+        _dev(dv, "dv")
+    B, C, H, W = qkv.shape
+    if C != 4 * heads * key_dim:
+        raise ValueError(f"qkv has {C} channels, expected 4*heads*key_dim = {4 * heads * key_dim}")
+    lib = load_library()
+    if dqkv is None:
+        dqkv = torch.empty_like(qkv)
+    if workspace is None:
+        nbytes = lib.psa_attention_bwd_workspace_bytes(B, heads, H, W)
+        workspace = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=qkv.device)
+    s = default_scale(key_dim) if scale is None else float(scale)
+    _check(lib.psa_attention_bwd(qkv.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                 _ptr(dv), _dev(dqkv, "dqkv").data_ptr(), _dev(workspace, "workspace").data_ptr(),
+                                 B, heads, key_dim, H, W, s, _dtype_code(qkv), _stream(qkv)))
+    return dqkv
 
 
 def psa_abi_version() -> int:

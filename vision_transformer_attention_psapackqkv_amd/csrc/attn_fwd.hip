@@ -55,9 +55,6 @@ constexpr int kBN = 64;   // keys per tile
 constexpr int kWavesFwd = 4;   // waves per workgroup, 32 queries each
 constexpr int kPad = 8;   // bf16 elements of padding per LDS row (spreads banks)
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
 struct FwdArgs {
   const uint16_t* q;   // packed: [BH, n_q, KD]; NCHW: the qkv tensor
   const uint16_t* k;   // packed: [BH, n_k, KD]; NCHW: the qkv tensor
@@ -101,32 +98,6 @@ __device__ __forceinline__ int split_tile(const FwdArgs& a, int s) {
   return a.full + s;
 }
 
-__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
-
-__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-// 8 bf16 values p[0], p[stride], ..., p[7*stride], zero where idx0 + e >= limit.
-__device__ __forceinline__ u32x4 gather8(const uint16_t* p, int64_t stride, int idx0, int limit) {
-  u32x4 r;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = (idx0 + 2 * w < limit) ? p[(2 * w) * stride] : 0u;
-    const uint32_t hi = (idx0 + 2 * w + 1 < limit) ? p[(2 * w + 1) * stride] : 0u;
-    r[w] = lo | (hi << 16);
-  }
-  return r;
-}
-
-// Two ds_read_b64_tr_b16 (rows p[0..3] and p[4*row..]) forming one 8-value operand.
-__device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* p, int row) {
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * row));
-  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-}
-
 // Value of x held by lane ^ 32 (g = lane / 32): one v_permlane32_swap, which
 // leaves the partner's value in the first result on the upper half-wave and
 // in the second on the lower.
@@ -135,17 +106,6 @@ __device__ __forceinline__ float lane_xor32(float x, int g) {
       __builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false));
   return __builtin_bit_cast(float, g ? sw[0] : sw[1]);
 }
-
-// Key held by S^T row rho (0..31) of a 32-key block: 8h + 4g + e -> 8g + 4h + e
-// inside each 16-row half.
-__device__ __forceinline__ int key_of_row(int rho) {
-  return (rho & 16) | ((rho & 4) << 1) | ((rho & 8) >> 1) | (rho & 3);
-}
-
-// Column offset (in keys) a 16-lane group's source lane s supplies for the
-// transposed K read, so that output lane i receives key key_of_row(i).
-__device__ __forceinline__ int tr_key_col(int s) { return ((s & 1) << 3) | ((s & 2) << 1); }
-
 
 template <int KD, int DV, bool kNCHW, int kWaves, bool kDirect>
 struct FwdCfg {
@@ -176,11 +136,6 @@ struct FwdCfg {
 constexpr int kMaxSplits = 6;
 constexpr int kSplitMinTiles = 16;
 
-// Position of 16-byte chunk c (8 keys) of V row dv in the unpadded, directly
-// staged V tile: an XOR swizzle that puts the 16 rows read together by one
-// 16-byte-per-lane instruction on 16 different bank groups.
-__device__ __forceinline__ int v_chunk_pos(int dv, int c) { return c ^ ((dv >> 1) & 7); }
-
 // Direct global -> LDS staging of one NCHW key tile (N a multiple of 8): each
 // wave instruction (global_load_lds_dwordx4) fills 64 consecutive 16-byte LDS
 // chunks, lane i the i-th; lanes pick which global chunk to fetch, which is
@@ -205,7 +160,7 @@ struct FwdStageDirect {
       const bool is_k = b < K_BLOCKS;
       const int q = is_k ? p : p - K_BLOCKS * 64;
       const int row = q >> 3;                      // d (K) or dv (V)
-      const int c = is_k ? (q & 7) : v_chunk_pos(row, q & 7);
+      const int c = is_k ? (q & 7) : tile_chunk_pos(row, q & 7);
       int m = m0 + c * 8;
       m = m < N ? m : N - 8;                       // keys past n_k: real data, masked later
       const int64_t ch = static_cast<int64_t>(bh) * 4 * KD + (is_k ? KD : 2 * KD) + row;
@@ -460,7 +415,7 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
         bf16x8 vop;
         if constexpr (kDirect)
           vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW +
-                                                 v_chunk_pos(db * 32 + l32, 2 * s + g) * 8);
+                                                 tile_chunk_pos(db * 32 + l32, 2 * s + g) * 8);
         else if constexpr (kNCHW)
           vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW + s * 16 + g * 8);
         else

@@ -1,0 +1,490 @@
+// PSA backward for gfx950: the gradient of the fused PSA forward with respect
+// to the NCHW QKV tensor, computed as one dual-V Flash Attention 2 backward.
+//
+// vision-rs book, "Custom Kernels", sections "Position-Sensitive Attention
+// (PSA)" and "Flash Attention 2". The forward's output is [O_lo | O_hi] with
+// O_j = softmax(s Q K^T) V_j, plus the V residual (a copy of the V channels).
+// Both halves share P = softmax(s Q K^T), so with V = [V_lo | V_hi] and
+// dO = [dO_lo | dO_hi] (value width DV = 2*KEY_DIM) the sum over the halves
+// of each half's FA2 backward is one backward of width DV:
+//   Delta = rowsum(dO * O)             (over both halves)
+//   dS    = P * (dO V^T - Delta)       (one dS serves both halves)
+//   dV    = P^T dO + dV_residual,   dK = s dS^T Q,   dQ = s dS K.
+// Like the page's FA2 backward, dQ and dK/dV are separate kernels with their
+// own grids (no atomics):
+//   psa_bwd_prep: Delta and LSE * log2(e) per (bh, pixel);
+//   psa_bwd_dkdv: one workgroup per (bh, 128 keys), looping over 64-query tiles;
+//   psa_bwd_dq:   one workgroup per (bh, 128 queries), looping over 64-key tiles.
+// Every tensor is read and written in NCHW (channel rows of N pixels), so the
+// split, pack and unpack permutations of an unfused chain never run.
+//
+// dK/dV kernel, per wave (32 keys) and 32-query block; the wave's K and V rows
+// are register operands:
+//   S [q][key] = Q K^T          A = Q  (LDS [d][q] tile, transposed read)
+//   dP[q][key] = dO V^T         A = dO (LDS [dv][q] tile, transposed read)
+//   dV^T[dv][key] += dO^T P     A = dO^T (LDS, 16-byte read), B = P (registers)
+//   dK^T[d][key]  += Q^T dS     A = Q^T  (LDS, 16-byte read), B = dS (registers)
+// dQ kernel, per wave (32 queries) and 32-key block; Q and dO rows in registers:
+//   S^T [key][q] = K Q^T        A = K (LDS [d][key] tile, transposed read)
+//   dP^T[key][q] = V dO^T       A = V (LDS [dv][key] tile, transposed read)
+//   dQ^T[d][q]  += K^T dS^T     A = K^T (LDS, 16-byte read), B = dS^T (registers)
+// The transposed reads permute the rows of the first products (key_of_row), so
+// the accumulator a lane holds is directly the B operand of the last product.
+// LDS tiles are unpadded rows of 64 pixels with XOR-swizzled 16-byte chunks
+// (tile_chunk_pos), read both ways; they are filled straight from global memory
+// (global_load_lds_dwordx4) when N is a multiple of 8, through registers
+// otherwise. Scores use base 2: P = 2^(S * s*log2(e) - LSE*log2(e)).
+#include <math.h>
+
+#include "psa_device.hpp"
+#include "psa_launch.hpp"
+
+namespace psa {
+namespace {
+
+constexpr int kTN = 64;        // pixels per LDS tile (queries or keys)
+constexpr int kWavesBwd = 4;   // 32 rows (keys or queries) per wave
+constexpr int kThreadsBwd = kWavesBwd * 64;
+
+struct PsaBwdArgs {
+  const uint16_t* qkv;    // [BH * 4KD, N]: per head Q, K, V_lo, V_hi channel rows
+  const uint16_t* o;      // [BH * DV, N]
+  const uint16_t* dout;   // [BH * DV, N]
+  const uint16_t* dvres;  // [BH * DV, N] or null
+  const float* lse;       // [BH, N], natural log
+  float* delta;           // [BH, N]
+  float* lse2;            // [BH, N]: LSE * log2(e)
+  uint16_t* dqkv;         // [BH * 4KD, N]
+  int BH, N, tiles;       // tiles: workgroups per batch-head
+  float scale, c;         // s and s * log2(e)
+};
+
+// blockIdx -> (bh, tile) with each XCD given a contiguous run of tiles
+// (workgroups are dispatched round-robin over the 8 XCDs).
+__device__ __forceinline__ void xcd_tile(int total, int tiles, int& bh, int& t) {
+  const int i = blockIdx.x;
+  const int per = total / 8;
+  const int L = (i < per * 8) ? (i % 8) * per + i / 8 : i;
+  bh = L / tiles;
+  t = L - bh * tiles;
+}
+
+// Element (row, col) of a swizzled [rows][64] LDS tile.
+__device__ __forceinline__ const uint16_t* tile_at(const uint16_t* tile, int row, int col) {
+  return tile + row * kTN + tile_chunk_pos(row, col >> 3) * 8 + (col & 7);
+}
+
+// One operand of 8 values down rows r0 .. r0+7 at column col of a swizzled tile:
+// two ds_read_b64_tr_b16 (rows r0.. and r0+4..), see lds_read_tr8.
+__device__ __forceinline__ bf16x8 tile_read_tr8(const uint16_t* tile, int r0, int col) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tile_at(tile, r0, col));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tile_at(tile, r0 + 4, col));
+  const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+  return as_bf16x8(u32x4{x[0], x[1], y[0], y[1]});
+}
+
+// 8 consecutive columns (one 16-byte chunk) of row `row` of a swizzled tile.
+__device__ __forceinline__ bf16x8 tile_read8(const uint16_t* tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * kTN + tile_chunk_pos(row, chunk) * 8);
+}
+
+// Rows [0, R) x pixels [m0, m0 + 64) of an NCHW slab (row r at src + r*N) into a
+// swizzled LDS tile, straight from global memory: wave instruction b fills the
+// 1 KB of rows 8b .. 8b+7, lane i the i-th 16-byte chunk, fetching the pixel
+// chunk the swizzle puts there. Pixels past N repeat real data (the kernels
+// give them zero weight). Needs N a multiple of 8.
+template <int R>
+__device__ __forceinline__ void stage_direct(const uint16_t* src, int N, int m0, int wave, int lane,
+                                             uint16_t* dst) {
+  constexpr int BLOCKS = R / 8;
+  static_assert(R % 8 == 0, "whole 1 KB blocks");
+#pragma unroll
+  for (int i = 0; i < (BLOCKS + kWavesBwd - 1) / kWavesBwd; ++i) {
+    const int b = wave + i * kWavesBwd;
+    if (b >= BLOCKS) break;
+    const int row = b * 8 + (lane >> 3);
+    int m = m0 + tile_chunk_pos(row, lane & 7) * 8;
+    m = m < N ? m : N - 8;
+    __builtin_amdgcn_global_load_lds(src + static_cast<int64_t>(row) * N + m,
+                                     (__attribute__((address_space(3))) void*)(dst + b * 512), 16, 0, 0);
+  }
+}
+
+// The same tile through registers, for any N (pixels past N read as zero).
+template <int R>
+struct StageRegs {
+  static constexpr int CH = R * 8;   // 16-byte chunks
+  static constexpr int PER = (CH + kThreadsBwd - 1) / kThreadsBwd;
+  u32x4 r[PER];
+
+  __device__ __forceinline__ void load(const uint16_t* src, int N, int m0, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * kThreadsBwd;
+      if (c < CH) {
+        const int row = c >> 3;
+        const int m = m0 + tile_chunk_pos(row, c & 7) * 8;
+        r[i] = gather8(src + static_cast<int64_t>(row) * N + m, 1, m, N);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * kThreadsBwd;
+      if (c < CH) *reinterpret_cast<u32x4*>(dst + c * 8) = r[i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------- prep
+
+template <int DV>
+__global__ __launch_bounds__(256) void psa_bwd_prep(PsaBwdArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(a.BH) * a.N) return;
+  const int64_t bh = idx / a.N;
+  const int64_t n = idx - bh * a.N;
+  const uint16_t* o = a.o + bh * DV * a.N + n;
+  const uint16_t* g = a.dout + bh * DV * a.N + n;
+  float acc = 0.0f;
+#pragma unroll 8
+  for (int dv = 0; dv < DV; ++dv)
+    acc = fmaf(bf16_bits_to_float(o[static_cast<int64_t>(dv) * a.N]),
+               bf16_bits_to_float(g[static_cast<int64_t>(dv) * a.N]), acc);
+  a.delta[idx] = acc;
+  a.lse2[idx] = a.lse[idx] * kLog2e;
+}
+
+// ---------------------------------------------------------------- dK / dV
+
+template <int KD, bool kVecN, int kOcc>
+__global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) {
+  constexpr int DV = 2 * KD;
+  constexpr int DP = KD < 32 ? 32 : KD;   // Q tile rows (one MFMA block minimum)
+  constexpr int NDS = KD / 16, NVS = DV / 16;
+  constexpr int NDK = DP / 32, NDV = DV / 32;
+  constexpr int Q_EL = DP * kTN, DO_EL = DV * kTN;
+  constexpr int BUF = Q_EL + DO_EL + 2 * kTN * 2;   // + LSE*log2(e) and Delta (floats)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int i16 = lane & 15, t16 = (lane >> 4) & 1;
+  const int N = a.N;
+  int bh, kt;
+  xcd_tile(a.BH * a.tiles, a.tiles, bh, kt);
+  const int key = kt * 32 * kWavesBwd + wave * 32 + l32;
+  const bool k_ok = key < N;
+  const uint16_t* qkv = a.qkv + static_cast<int64_t>(bh) * 4 * KD * N;
+  const uint16_t* dout = a.dout + static_cast<int64_t>(bh) * DV * N;
+
+  if constexpr (DP > KD) {   // Q tile rows KD..DP-1 stay zero
+    for (int e = tid; e < (DP - KD) * kTN; e += kThreadsBwd) {
+      smem[KD * kTN + e] = 0;
+      smem[BUF + KD * kTN + e] = 0;
+    }
+  }
+
+  // B operands of S and dP: K[key][16ds + 8g + j] and V[key][16vs + 8g + j].
+  bf16x8 kop[NDS], vop[NVS];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds)
+    kop[ds] = as_bf16x8(k_ok ? gather8(qkv + static_cast<int64_t>(KD + ds * 16 + g * 8) * N + key, N, 0, 8)
+                             : zero4());
+#pragma unroll
+  for (int vs = 0; vs < NVS; ++vs)
+    vop[vs] = as_bf16x8(k_ok ? gather8(qkv + static_cast<int64_t>(2 * KD + vs * 16 + g * 8) * N + key, N, 0, 8)
+                             : zero4());
+  f32x16 dk[NDK], dv[NDV];
+#pragma unroll
+  for (int b = 0; b < NDK; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[b][r] = 0.0f;
+#pragma unroll
+  for (int b = 0; b < NDV; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[b][r] = 0.0f;
+
+  // Per query tile: Q rows, dO rows, and (threads 0..127) LSE*log2(e) / Delta.
+  StageRegs<KD> sq;
+  StageRegs<DV> sg;
+  float fval = 0.0f;
+  auto issue = [&](int t, uint16_t* buf) {
+    const int q0 = t * kTN;
+    if constexpr (kVecN) {
+      stage_direct<KD>(qkv, N, q0, wave, lane, buf);
+      stage_direct<DV>(dout, N, q0, wave, lane, buf + Q_EL);
+    } else {
+      sq.load(qkv, N, q0, tid);
+      sg.load(dout, N, q0, tid);
+    }
+    if (tid < 2 * kTN) {
+      const int q = q0 + (tid & (kTN - 1));
+      const bool ok = q < N;
+      const int64_t i = static_cast<int64_t>(bh) * N + q;
+      // queries past N: P = 2^-inf = 0
+      fval = tid < kTN ? (ok ? a.lse2[i] : INFINITY) : (ok ? a.delta[i] : 0.0f);
+    }
+  };
+  auto finish = [&](uint16_t* buf) {
+    if constexpr (kVecN) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      sq.store(buf, tid);
+      sg.store(buf + Q_EL, tid);
+    }
+    if (tid < 2 * kTN) reinterpret_cast<float*>(buf + Q_EL + DO_EL)[tid] = fval;
+  };
+
+  const int n_tiles = (N + kTN - 1) / kTN;
+  issue(0, smem);
+  finish(smem);
+  __syncthreads();
+
+  for (int qt = 0; qt < n_tiles; ++qt) {
+    const uint16_t* qs = smem + (qt & 1) * BUF;
+    const uint16_t* gs = qs + Q_EL;
+    const float* fl = reinterpret_cast<const float*>(gs + DO_EL);
+    const bool more = qt + 1 < n_tiles;
+    if (more) issue(qt + 1, smem + ((qt + 1) & 1) * BUF);
+
+#pragma unroll
+    for (int qb = 0; qb < kTN / 32; ++qb) {
+      // Rows of S and dP: query qb*32 + 16*(r/8) + 8g + r%8 in element r.
+      const int col = qb * 32 + 16 * t16 + tr_key_col(i16 & 3);
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds)
+        sacc = mfma32x32x16(tile_read_tr8(qs, ds * 16 + 8 * g + (i16 >> 2), col), kop[ds], sacc);
+#pragma unroll
+      for (int vs = 0; vs < NVS; ++vs)
+        pacc = mfma32x32x16(tile_read_tr8(gs, vs * 16 + 8 * g + (i16 >> 2), col), vop[vs], pacc);
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = qb * 32 + 16 * h + 8 * g;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(fl + q);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(fl + q + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(fl + kTN + q);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(fl + kTN + q + 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * h + j;
+          const float l2 = j < 4 ? l0[j] : l1[j - 4];
+          const float dl = j < 4 ? d0[j] : d1[j - 4];
+          const float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
+          pb[h][j] = static_cast<__bf16>(p);
+          sb[h][j] = static_cast<__bf16>(p * (pacc[r] - dl));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's queries, 16 per step.
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int b = 0; b < NDV; ++b)
+          dv[b] = mfma32x32x16(tile_read8(gs, b * 32 + l32, 4 * qb + 2 * s + g), pb[s], dv[b]);
+#pragma unroll
+        for (int b = 0; b < NDK; ++b)
+          dk[b] = mfma32x32x16(tile_read8(qs, b * 32 + l32, 4 * qb + 2 * s + g), sb[s], dk[b]);
+      }
+    }
+    if (more) finish(smem + ((qt + 1) & 1) * BUF);
+    __syncthreads();
+  }
+
+  if (!k_ok) return;
+  uint16_t* dq_out = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N;
+  // dK^T / dV^T element r: row 32b + 8(r/4) + 4g + r%4, column = this lane's key.
+#pragma unroll
+  for (int b = 0; b < NDK; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = b * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (d < KD) dq_out[static_cast<int64_t>(KD + d) * N + key] = float_to_bf16_bits(dk[b][r] * a.scale);
+    }
+  const uint16_t* dvres = a.dvres ? a.dvres + static_cast<int64_t>(bh) * DV * N : nullptr;
+#pragma unroll
+  for (int b = 0; b < NDV; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = b * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      float x = dv[b][r];
+      if (dvres) x += bf16_bits_to_float(dvres[static_cast<int64_t>(d) * N + key]);
+      dq_out[static_cast<int64_t>(2 * KD + d) * N + key] = float_to_bf16_bits(x);
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int KD, bool kVecN, int kOcc>
+__global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
+  constexpr int DV = 2 * KD;
+  constexpr int DP = KD < 32 ? 32 : KD;   // K tile rows (one MFMA block minimum)
+  constexpr int NDS = KD / 16, NVS = DV / 16, NDB = DP / 32;
+  constexpr int K_EL = DP * kTN, V_EL = DV * kTN;
+  constexpr int BUF = K_EL + V_EL;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int i16 = lane & 15, t16 = (lane >> 4) & 1;
+  const int N = a.N;
+  int bh, qt;
+  xcd_tile(a.BH * a.tiles, a.tiles, bh, qt);
+  const int q = qt * 32 * kWavesBwd + wave * 32 + l32;
+  const bool q_ok = q < N;
+  const uint16_t* qkv = a.qkv + static_cast<int64_t>(bh) * 4 * KD * N;
+  const uint16_t* dout = a.dout + static_cast<int64_t>(bh) * DV * N;
+
+  if constexpr (DP > KD) {   // K tile rows KD..DP-1 stay zero
+    for (int e = tid; e < (DP - KD) * kTN; e += kThreadsBwd) {
+      smem[KD * kTN + e] = 0;
+      smem[BUF + KD * kTN + e] = 0;
+    }
+  }
+
+  // B operands: Q[q][16ds + 8g + j] and dO[q][16vs + 8g + j].
+  bf16x8 qop[NDS], gop[NVS];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds)
+    qop[ds] = as_bf16x8(q_ok ? gather8(qkv + static_cast<int64_t>(ds * 16 + g * 8) * N + q, N, 0, 8) : zero4());
+#pragma unroll
+  for (int vs = 0; vs < NVS; ++vs)
+    gop[vs] = as_bf16x8(q_ok ? gather8(dout + static_cast<int64_t>(vs * 16 + g * 8) * N + q, N, 0, 8) : zero4());
+  const float l2 = q_ok ? a.lse2[static_cast<int64_t>(bh) * N + q] : INFINITY;
+  const float dl = q_ok ? a.delta[static_cast<int64_t>(bh) * N + q] : 0.0f;
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[b][r] = 0.0f;
+
+  StageRegs<KD> sk;
+  StageRegs<DV> sv;
+  auto issue = [&](int t, uint16_t* buf) {
+    if constexpr (kVecN) {
+      stage_direct<KD>(qkv + static_cast<int64_t>(KD) * N, N, t * kTN, wave, lane, buf);
+      stage_direct<DV>(qkv + static_cast<int64_t>(2 * KD) * N, N, t * kTN, wave, lane, buf + K_EL);
+    } else {
+      sk.load(qkv + static_cast<int64_t>(KD) * N, N, t * kTN, tid);
+      sv.load(qkv + static_cast<int64_t>(2 * KD) * N, N, t * kTN, tid);
+    }
+  };
+  auto finish = [&](uint16_t* buf) {
+    if constexpr (kVecN) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      sk.store(buf, tid);
+      sv.store(buf + K_EL, tid);
+    }
+  };
+
+  const int n_tiles = (N + kTN - 1) / kTN;
+  issue(0, smem);
+  finish(smem);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const uint16_t* ks = smem + (kt & 1) * BUF;
+    const uint16_t* vs_ = ks + K_EL;
+    const bool more = kt + 1 < n_tiles;
+    if (more) issue(kt + 1, smem + ((kt + 1) & 1) * BUF);
+
+    bf16x8 sb[kTN / 16];   // dS^T, 16 keys per step
+#pragma unroll
+    for (int kb = 0; kb < kTN / 32; ++kb) {
+      // Rows of S^T and dP^T: key kb*32 + 16*(r/8) + 8g + r%8 in element r.
+      const int col = kb * 32 + 16 * t16 + tr_key_col(i16 & 3);
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds)
+        sacc = mfma32x32x16(tile_read_tr8(ks, ds * 16 + 8 * g + (i16 >> 2), col), qop[ds], sacc);
+#pragma unroll
+      for (int vs = 0; vs < NVS; ++vs)
+        pacc = mfma32x32x16(tile_read_tr8(vs_, vs * 16 + 8 * g + (i16 >> 2), col), gop[vs], pacc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt * kTN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+        float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
+        if (key >= N) p = 0.0f;
+        sb[kb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pacc[r] - dl));
+      }
+    }
+    // dQ^T += K^T dS^T over the tile's keys, 16 per step.
+#pragma unroll
+    for (int s = 0; s < kTN / 16; ++s)
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) dq[b] = mfma32x32x16(tile_read8(ks, b * 32 + l32, 2 * s + g), sb[s], dq[b]);
+
+    if (more) finish(smem + ((kt + 1) & 1) * BUF);
+    __syncthreads();
+  }
+
+  if (!q_ok) return;
+  uint16_t* dq_out = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N;
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = b * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (d < KD) dq_out[static_cast<int64_t>(d) * N + q] = float_to_bf16_bits(dq[b][r] * a.scale);
+    }
+}
+
+template <int KD>
+hipError_t run_psa_bwd(PsaBwdArgs a, hipStream_t stream) {
+  // Two workgroups per CU fit the registers up to key_dim 32; the dK/dV
+  // kernel's accumulators (dK^T and the 2*KD-wide dV^T) need a whole SIMD's
+  // register file from key_dim 64 on.
+  constexpr int kOccDkdv = KD <= 32 ? 2 : 1;
+  constexpr int kOccDq = KD <= 64 ? 2 : 1;
+  const int64_t rows = static_cast<int64_t>(a.BH) * a.N;
+  psa_bwd_prep<2 * KD><<<dim3(static_cast<unsigned>((rows + 255) / 256)), 256, 0, stream>>>(a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  a.tiles = (a.N + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
+  const dim3 grid(static_cast<unsigned>(a.BH) * a.tiles);
+  const bool vec_n = a.N % 8 == 0;
+  if (vec_n)
+    psa_bwd_dkdv<KD, true, kOccDkdv><<<grid, kThreadsBwd, 0, stream>>>(a);
+  else
+    psa_bwd_dkdv<KD, false, kOccDkdv><<<grid, kThreadsBwd, 0, stream>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (vec_n)
+    psa_bwd_dq<KD, true, kOccDq><<<grid, kThreadsBwd, 0, stream>>>(a);
+  else   // the register-staged tiles need more registers
+    psa_bwd_dq<KD, false, KD <= 32 ? 2 : 1><<<grid, kThreadsBwd, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_psa_fused_bwd(const void* qkv, const void* out, const float* lse, const void* dout,
+                                const void* dvres, void* dqkv, float* workspace, int BH, int KD,
+                                int N, float scale, hipStream_t stream) {
+  PsaBwdArgs a{};
+  a.qkv = static_cast<const uint16_t*>(qkv);
+  a.o = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dvres = static_cast<const uint16_t*>(dvres);
+  a.lse = lse;
+  a.delta = workspace;
+  a.lse2 = workspace + static_cast<int64_t>(BH) * N;
+  a.dqkv = static_cast<uint16_t*>(dqkv);
+  a.BH = BH;
+  a.N = N;
+  a.scale = scale;
+  a.c = scale * kLog2e;
+  switch (KD) {
+    case 16: return run_psa_bwd<16>(a, stream);
+    case 32: return run_psa_bwd<32>(a, stream);
+    case 64: return run_psa_bwd<64>(a, stream);
+    case 128: return run_psa_bwd<128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace psa

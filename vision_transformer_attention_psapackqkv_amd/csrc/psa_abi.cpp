@@ -273,6 +273,48 @@ psa_status psa_attention_fwd(const void* qkv_nchw, void* out_nchw, void* v_nchw,
                                                 as_stream(stream)));
 }
 
+size_t psa_attention_bwd_workspace_bytes(int B, int heads, int H, int W) {
+  if (B <= 0 || heads <= 0 || H <= 0 || W <= 0) return 0;
+  return 2 * static_cast<size_t>(B) * heads * H * W * sizeof(float);
+}
+
+psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const float* lse,
+                             const void* dout_nchw, const void* dv_nchw, void* dqkv_nchw,
+                             float* workspace, int B, int heads, int key_dim, int H, int W,
+                             float scale, psa_dtype dtype, void* stream) {
+  const char* fn = "psa_attention_bwd";
+  if (!qkv_nchw || !out_nchw || !lse || !dout_nchw || !dqkv_nchw || !workspace)
+    return fail(PSA_ERR_NULL, fn, "qkv_nchw, out_nchw, lse, dout_nchw, dqkv_nchw and workspace "
+                                  "must not be NULL (dv_nchw may be)");
+  PSA_TRY(check_map(fn, B, heads, key_dim, H, W, dtype));
+  if (dtype != PSA_BF16)
+    return fail(PSA_ERR_UNSUPPORTED, fn, "dtype=%d: only PSA_BF16 (1) is built for the backward",
+                static_cast<int>(dtype));
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(PSA_ERR_UNSUPPORTED, fn, "scale=%g must be finite and > 0", static_cast<double>(scale));
+  const char* names[7] = {"qkv_nchw", "out_nchw", "lse", "dout_nchw", "dv_nchw", "dqkv_nchw", "workspace"};
+  const void* ptrs[7] = {qkv_nchw, out_nchw, lse, dout_nchw, dv_nchw, dqkv_nchw, workspace};
+  for (int i = 0; i < 7; ++i)
+    if (ptrs[i]) PSA_TRY(check_aligned(fn, names[i], ptrs[i]));
+  const int64_t eb = elt_bytes(dtype);
+  const int64_t half = static_cast<int64_t>(B) * heads * key_dim * H * W;
+  const int64_t rows = static_cast<int64_t>(B) * heads * H * W;
+  const Range outs[2] = {range("dqkv_nchw", dqkv_nchw, 4 * half, eb),
+                         range("workspace", workspace, 2 * rows, 4)};
+  const Range ins[5] = {range("qkv_nchw", qkv_nchw, 4 * half, eb), range("out_nchw", out_nchw, 2 * half, eb),
+                        range("lse", lse, rows, 4), range("dout_nchw", dout_nchw, 2 * half, eb),
+                        range("dv_nchw", dv_nchw, dv_nchw ? 2 * half : 0, eb)};
+  PSA_TRY(check_disjoint(fn, outs, 2));
+  for (const Range& a : outs)
+    for (const Range& b : ins) {
+      const Range pair[2] = {a, b};
+      PSA_TRY(check_disjoint(fn, pair, 2));
+    }
+  return launched(fn, psa::launch_psa_fused_bwd(qkv_nchw, out_nchw, lse, dout_nchw, dv_nchw,
+                                                dqkv_nchw, workspace, B * heads, key_dim, H * W,
+                                                scale, as_stream(stream)));
+}
+
 const char* psa_last_error(void) { return g_last_error.c_str(); }
 
 int psa_abi_version(void) { return PSA_ABI_VERSION; }

@@ -37,6 +37,55 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// 8 bf16 values p[0], p[stride], ..., p[7*stride], zero where idx0 + e >= limit.
+__device__ __forceinline__ u32x4 gather8(const uint16_t* p, int64_t stride, int idx0, int limit) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = (idx0 + 2 * w < limit) ? p[(2 * w) * stride] : 0u;
+    const uint32_t hi = (idx0 + 2 * w + 1 < limit) ? p[(2 * w + 1) * stride] : 0u;
+    r[w] = lo | (hi << 16);
+  }
+  return r;
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// One MFMA operand (8 values along LDS rows) from two ds_read_b64_tr_b16: each
+// reads 8 bytes per lane, and inside each 16-lane group output lane i receives
+// element i%4 of the 8 bytes addressed by lane 4r + i/4 (r = 0..3), a 4x16
+// transpose. The second read is 4 rows (`row` elements per row) further on.
+__device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* p, int row) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * row));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+}
+
+// Index held by row rho (0..31) of a 32-row accumulator block whose A operand
+// was read with tr_key_col: 8h + 4g + e -> 8g + 4h + e inside each 16-row half.
+// Accumulator element r of lane group g then holds index 16*(r/8) + 8g + r%8:
+// 8 consecutive indices per 8 elements, ready to be a B operand over them.
+__device__ __forceinline__ int key_of_row(int rho) {
+  return (rho & 16) | ((rho & 4) << 1) | ((rho & 8) >> 1) | (rho & 3);
+}
+
+// Column offset a 16-lane group's source lane s supplies for a transposed
+// read, so that output lane i receives index key_of_row(i).
+__device__ __forceinline__ int tr_key_col(int s) { return ((s & 1) << 3) | ((s & 2) << 1); }
+
+// Position of 16-byte chunk c of row `row` in an unpadded LDS tile of 64
+// bf16 columns: an XOR swizzle that puts the 16 rows one 16-byte-per-lane
+// instruction reads together on 16 different bank groups.
+__device__ __forceinline__ int tile_chunk_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
+
 template <typename T>
 __device__ __forceinline__ T ldg_nt(const T* p) { return __builtin_nontemporal_load(p); }
 template <typename T>
