@@ -10,7 +10,7 @@ throughput in TFLOP/s, counting the algorithmic 6*BH*N^2*KEY_DIM flops
 Also measured and reported in the same JSON line: the unfused chain (pack,
 FA2 x2, merge, extract), the layout kernels' GB/s against HBM peak (input and
 output buffers rotated over 4 sets larger than the 256 MB Infinity Cache), the
-40x40 forward and the FA2 backward workload. The CPU oracle is timed on a
+40x40 forward, the FA2 backward workload and the PSA backward on the 40x40 map. The CPU oracle is timed on a
 bounded sample of the same workload as a reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -46,6 +46,8 @@ def parse_args():
                     help="time only the fused step (for profiler runs)")
     ap.add_argument("--layout-only", action="store_true",
                     help="only run pack, merge and extract a few times (for profiler runs)")
+    ap.add_argument("--psa-bwd-only", action="store_true",
+                    help="time only the PSA backward on the 40x40 map (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy 3 times (HBM counter calibration)")
     return ap.parse_args()
@@ -140,6 +142,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes_read": src.numel() * 2,
                           "calibration_copy_bytes_written": dst.numel() * 2}))
+        return
+    if args.psa_bwd_only:
+        print(json.dumps({"psa_bwd_40x40": psa_bwd_component(torch, psa, I, dev, args.steps, args.warmup)}))
         return
     w = I.WORKLOADS[WORKLOAD]
     qkv_cpu = I.make_workload_qkv(w)
@@ -282,7 +287,27 @@ def components(torch, psa, I, w, qkv, args):
     comp["fa2_bwd_40x40"] = {"avg_ms": round(avg, 5), "TFLOP/s": round(tb, 3),
                              "pct_bf16_mfma_peak": round(100 * tb / PEAK_BF16_TFLOPS, 2),
                              "flops": "10*BH*N^2*D"}
+    del q, k, v, do, o, lse_b, ws
+    comp["psa_bwd_40x40"] = psa_bwd_component(torch, psa, I, dev, steps, warm)
     return comp
+
+
+def psa_bwd_component(torch, psa, I, dev, steps, warm):
+    """The PSA backward (psa_attention_bwd: d(qkv) from dOut and the V-residual gradient) on
+    the 40x40 forward map, O and LSE from the fused forward."""
+    w = I.WORKLOADS["psa_fwd_bf16_40x40_peaked"]
+    x = I.make_workload_qkv(w).to(dev)
+    out, _, lse = psa.psa_attention_fwd(x, w.heads, w.key_dim, want_v=False)
+    g = torch.randn(out.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev).to(out.dtype)
+    gv = torch.randn(out.shape, generator=torch.Generator(device=dev).manual_seed(8), device=dev).to(out.dtype)
+    dqkv = torch.empty_like(x)
+    ws = torch.empty((psa.load_library().psa_attention_bwd_workspace_bytes(w.B, w.heads, w.H, w.W) // 4,),
+                     dtype=torch.float32, device=dev)
+    avg, _, _ = time_events(lambda i: psa.psa_attention_bwd(x, out, lse, g, w.heads, w.key_dim, dv=gv,
+                                                            dqkv=dqkv, workspace=ws), steps, warm, torch)
+    t = 14.0 * w.BH * w.N ** 2 * w.key_dim / (avg * 1e-3) / 1e12
+    return {"avg_ms": round(avg, 5), "TFLOP/s": round(t, 3), "pct_bf16_mfma_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+            "flops": "14*BH*N^2*KD (QK^T, dO V^T over 2KD, P^T dO over 2KD, dS^T Q, dS K)"}
 
 
 if __name__ == "__main__":

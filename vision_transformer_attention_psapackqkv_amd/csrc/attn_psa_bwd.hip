@@ -248,13 +248,23 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
     const bool more = qt + 1 < n_tiles;
     if (more) issue(qt + 1, smem + ((qt + 1) & 1) * BUF);
 
-#pragma unroll
+#pragma unroll 1
     for (int qb = 0; qb < kTN / 32; ++qb) {
       // Rows of S and dP: query qb*32 + 16*(r/8) + 8g + r%8 in element r.
+      // dP's accumulator starts at -Delta, so it ends as dP - Delta.
       const int col = qb * 32 + 16 * t16 + tr_key_col(i16 & 3);
       f32x16 sacc, pacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+      for (int h = 0; h < 2; ++h) {
+        const int q = qb * 32 + 16 * h + 8 * g;
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(fl + kTN + q);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(fl + kTN + q + 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sacc[8 * h + j] = 0.0f;
+          pacc[8 * h + j] = -(j < 4 ? d0[j] : d1[j - 4]);
+        }
+      }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds)
         sacc = mfma32x32x16(tile_read_tr8(qs, ds * 16 + 8 * g + (i16 >> 2), col), kop[ds], sacc);
@@ -267,16 +277,12 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
         const int q = qb * 32 + 16 * h + 8 * g;
         const f32x4 l0 = *reinterpret_cast<const f32x4*>(fl + q);
         const f32x4 l1 = *reinterpret_cast<const f32x4*>(fl + q + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(fl + kTN + q);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(fl + kTN + q + 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * h + j;
-          const float l2 = j < 4 ? l0[j] : l1[j - 4];
-          const float dl = j < 4 ? d0[j] : d1[j - 4];
-          const float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
+          const float p = fast_exp2(fmaf(sacc[r], a.c, -(j < 4 ? l0[j] : l1[j - 4])));
           pb[h][j] = static_cast<__bf16>(p);
-          sb[h][j] = static_cast<__bf16>(p * (pacc[r] - dl));
+          sb[h][j] = static_cast<__bf16>(p * pacc[r]);
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the block's queries, 16 per step.
@@ -395,22 +401,30 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < kTN / 32; ++kb) {
       // Rows of S^T and dP^T: key kb*32 + 16*(r/8) + 8g + r%8 in element r.
+      // dP^T's accumulator starts at -Delta, so it ends as dP^T - Delta.
       const int col = kb * 32 + 16 * t16 + tr_key_col(i16 & 3);
       f32x16 sacc, pacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) {
+        sacc[r] = 0.0f;
+        pacc[r] = -dl;
+      }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds)
         sacc = mfma32x32x16(tile_read_tr8(ks, ds * 16 + 8 * g + (i16 >> 2), col), qop[ds], sacc);
 #pragma unroll
       for (int vs = 0; vs < NVS; ++vs)
         pacc = mfma32x32x16(tile_read_tr8(vs_, vs * 16 + 8 * g + (i16 >> 2), col), gop[vs], pacc);
+      // Keys past N (last tile only) get P = 0.
+      if ((kt + 1) * kTN > N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt * kTN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7) >= N) sacc[r] = -INFINITY;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kt * kTN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-        float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
-        if (key >= N) p = 0.0f;
-        sb[kb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pacc[r] - dl));
+        const float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
+        sb[kb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p * pacc[r]);
       }
     }
     // dQ^T += K^T dS^T over the tile's keys, 16 per step.
@@ -436,11 +450,11 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
 
 template <int KD>
 hipError_t run_psa_bwd(PsaBwdArgs a, hipStream_t stream) {
-  // Two workgroups per CU fit the registers up to key_dim 32; the dK/dV
-  // kernel's accumulators (dK^T and the 2*KD-wide dV^T) need a whole SIMD's
-  // register file from key_dim 64 on.
-  constexpr int kOccDkdv = KD <= 32 ? 2 : 1;
-  constexpr int kOccDq = KD <= 64 ? 2 : 1;
+  // Workgroups per CU the registers must allow: three up to key_dim 32, two at
+  // 64 (the dK/dV kernel walks its two 32-query blocks one after the other to
+  // stay in 256 registers); key_dim 128 needs a whole SIMD's register file.
+  constexpr int kOccDkdv = KD <= 32 ? 3 : KD <= 64 ? 2 : 1;
+  constexpr int kOccDq = KD <= 32 ? 3 : KD <= 64 ? 2 : 1;
   const int64_t rows = static_cast<int64_t>(a.BH) * a.N;
   psa_bwd_prep<2 * KD><<<dim3(static_cast<unsigned>((rows + 255) / 256)), 256, 0, stream>>>(a);
   hipError_t err = hipGetLastError();
@@ -450,8 +464,8 @@ hipError_t run_psa_bwd(PsaBwdArgs a, hipStream_t stream) {
   const bool vec_n = a.N % 8 == 0;
   if (vec_n)
     psa_bwd_dkdv<KD, true, kOccDkdv><<<grid, kThreadsBwd, 0, stream>>>(a);
-  else
-    psa_bwd_dkdv<KD, false, kOccDkdv><<<grid, kThreadsBwd, 0, stream>>>(a);
+  else   // the register-staged tiles need more registers
+    psa_bwd_dkdv<KD, false, KD <= 32 ? 3 : 1><<<grid, kThreadsBwd, 0, stream>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (vec_n)
     psa_bwd_dq<KD, true, kOccDq><<<grid, kThreadsBwd, 0, stream>>>(a);
