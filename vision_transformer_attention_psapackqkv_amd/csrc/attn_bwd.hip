@@ -167,8 +167,10 @@ struct DkdvTile {
   }
 };
 
+// Head dims up to 32: registers capped for three workgroups per CU (measured
+// faster than two with more registers).
 template <int D, int kWaves>
-__global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dkdv_bf16(BwdArgs a) {
   using Tile = DkdvTile<D, kWaves>;
   constexpr int BQ = Tile::BQ;
   constexpr int NDS = D / 16;
@@ -221,30 +223,36 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_bf16(BwdArgs a) {
 
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
-      // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries.
+      // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries, at the lane's
+      // queries qb*32 + 8*(r/4) + 4g + r%4; dP's accumulator starts at -Delta,
+      // so it ends as dP - Delta.
       f32x16 sacc, pacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(f + BQ + qb * 32 + 8 * r4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sacc[4 * r4 + e] = 0.0f;
+          pacc[4 * r4 + e] = -dl[e];
+        }
+      }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         const int off = (qb * 32 + l32) * Tile::RSTR + ds * 16 + g * 8;
         sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_Q + off), kop[ds], sacc);
         pacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_DO + off), vop[ds], pacc);
       }
-      // P and dS at the lane's queries qb*32 + 8*(r/4) + 4g + r%4.
+      // P and dS.
       bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int ql = qb * 32 + 8 * r4 + 4 * g;
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(f + ql);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(f + BQ + ql);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(f + qb * 32 + 8 * r4 + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
           const float p = fast_exp2(fmaf(sacc[r], a.c, -l2[e]));
-          const float dsv = p * (pacc[r] - dl[e]);
           pb[r >> 3][r & 7] = static_cast<__bf16>(p);
-          sb[r >> 3][r & 7] = static_cast<__bf16>(dsv);
+          sb[r >> 3][r & 7] = static_cast<__bf16>(p * pacc[r]);
         }
       }
       // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the 32 queries, 2 steps of 16).
@@ -347,7 +355,7 @@ struct DqTile {
 };
 
 template <int D, int kWaves>
-__global__ __launch_bounds__(kWaves * 64) void bwd_dq_bf16(BwdArgs a) {
+__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dq_bf16(BwdArgs a) {
   using Tile = DqTile<D, kWaves>;
   constexpr int BN = Tile::BN;
   constexpr int NDS = D / 16;
@@ -397,22 +405,30 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dq_bf16(BwdArgs a) {
     bf16x8 sb[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
-      // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T.
+      // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T (its accumulator starts at
+      // -Delta, so it ends as dP^T - Delta).
       f32x16 sacc, pacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) {
+        sacc[r] = 0.0f;
+        pacc[r] = -dl;
+      }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         const int off = (kb * 32 + l32) * Tile::RSTR + ds * 16 + g * 8;
         sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_K + off), qop[ds], sacc);
         pacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_V + off), gop[ds], pacc);
       }
+      // Keys past n_k (last tile only) get P = 0.
+      if ((kt + 1) * BN > a.n_k) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt * BN + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= a.n_k) sacc[r] = -INFINITY;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
-        if (key >= a.n_k) p = 0.0f;
-        sb[kb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p * (pacc[r] - dl));
+        const float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
+        sb[kb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p * pacc[r]);
       }
     }
     // dQ^T += K^T dS^T (reduction over the tile's keys).
