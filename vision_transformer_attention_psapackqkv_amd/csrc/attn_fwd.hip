@@ -146,26 +146,49 @@ struct FwdStageDirect {
   static constexpr int K_BLOCKS = KD * (kBN / 8) / 64;     // 1 KB blocks of K
   static constexpr int V_BLOCKS = DV * (kBN / 8) / 64;     // 1 KB blocks of V
   static constexpr int BLOCKS = K_BLOCKS + V_BLOCKS;
+  static constexpr int PER = (BLOCKS + kWaves - 1) / kWaves;   // blocks per wave
   static_assert(KD * (kBN / 8) % 64 == 0 && DV * (kBN / 8) % 64 == 0, "whole 1 KB blocks");
 
+  // Block b covers 8 channel rows starting at chan0(b) of the batch-head's
+  // [4*KD][N] slab; lane i fills LDS chunk i of it: row i/8 of the block, and
+  // the 8 keys the swizzle puts at position i%8.
+  __device__ static int chan0(int b) { return b < K_BLOCKS ? KD + 8 * b : 2 * KD + 8 * (b - K_BLOCKS); }
+  __device__ static int chunk(int b, int lane) {
+    const int r = lane >> 3;
+    return b < K_BLOCKS ? (lane & 7) : tile_chunk_pos(8 * (b - K_BLOCKS) + r, lane & 7);
+  }
+
+  uint32_t voff[PER];   // byte offset of this lane's 16 bytes from the block's (row, key) origin
+
+  __device__ __forceinline__ void init(int N, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int b = wave + i * kWaves;
+      voff[i] = b < BLOCKS ? static_cast<uint32_t>((lane >> 3) * N + chunk(b, lane) * 8) * 2u : 0u;
+    }
+  }
+
+  // `wave` must be wave-uniform (an SGPR value): block bases are then scalar
+  // and each load is a scalar base plus this lane's precomputed offset.
   __device__ __forceinline__ void issue(const FwdArgs& a, int bh, int kt, int wave, int lane,
                                         uint16_t* buf) const {
     const int N = a.n_k;
     const int m0 = kt * kBN;
+    const bool last = m0 + kBN > N;   // keys past n_k: clamped to real data, masked later
 #pragma unroll
-    for (int i = 0; i < (BLOCKS + kWaves - 1) / kWaves; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int b = wave + i * kWaves;
       if (b >= BLOCKS) break;
-      const int p = b * 64 + lane;                 // LDS chunk this lane fills
-      const bool is_k = b < K_BLOCKS;
-      const int q = is_k ? p : p - K_BLOCKS * 64;
-      const int row = q >> 3;                      // d (K) or dv (V)
-      const int c = is_k ? (q & 7) : tile_chunk_pos(row, q & 7);
-      int m = m0 + c * 8;
-      m = m < N ? m : N - 8;                       // keys past n_k: real data, masked later
-      const int64_t ch = static_cast<int64_t>(bh) * 4 * KD + (is_k ? KD : 2 * KD) + row;
-      __builtin_amdgcn_global_load_lds(a.k + ch * N + m,
-                                       (__attribute__((address_space(3))) void*)(buf + b * 512), 16, 0, 0);
+      const uint16_t* row0 = a.k + (static_cast<int64_t>(bh) * 4 * KD + chan0(b)) * N;
+      const uint16_t* src;
+      if (!last) {
+        src = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(row0 + m0) + voff[i]);
+      } else {
+        int m = m0 + chunk(b, lane) * 8;
+        m = m < N ? m : N - 8;
+        src = row0 + static_cast<int64_t>(lane >> 3) * N + m;
+      }
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + b * 512), 16, 0, 0);
     }
   }
 };
@@ -232,11 +255,15 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   constexpr int NKS = kBN / 16;        // 16-key MFMA steps per tile
   constexpr int NDS = KD / 16;         // 16-wide d steps of K Q^T
   constexpr int NDB = C::DVP / 32;     // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+  // Two tile buffers as two objects: the compiler can then tell that the
+  // direct global->LDS loads into one do not alias the LDS reads of the other,
+  // and does not make those reads wait for the loads.
+  __shared__ __attribute__((aligned(16))) uint16_t smem0[C::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t smem1[C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;           // lane group of the MFMA layouts
   const int i16 = lane & 15;         // lane inside its 16-lane group
@@ -273,8 +300,8 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   if constexpr (!kNCHW && C::DVP > DV) {
     for (int e = tid; e < kBN * (C::DVP - DV); e += NT) {
       const int row = e / (C::DVP - DV), col = DV + e % (C::DVP - DV);
-      smem[C::K_ELEMS + row * C::VROW + col] = 0;
-      smem[C::BUF + C::K_ELEMS + row * C::VROW + col] = 0;
+      smem0[C::K_ELEMS + row * C::VROW + col] = 0;
+      smem1[C::K_ELEMS + row * C::VROW + col] = 0;
     }
   }
 
@@ -326,20 +353,22 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   FwdStage<KD, DV, kNCHW, kVecN, kWaves> stage;
   FwdStageDirect<KD, DV, kWaves> dstage;
   if constexpr (kDirect) {
-    dstage.issue(a, bh, kt0, wave, lane, smem + (kt0 & 1) * C::BUF);
+    dstage.init(N, wave, lane);
+    dstage.issue(a, bh, kt0, wave, lane, smem0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
     stage.load(a, bh, kt0, tid);
-    stage.store(smem + (kt0 & 1) * C::BUF, tid);
+    stage.store(smem0, tid);
   }
   __syncthreads();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const uint16_t* ks = smem + (kt & 1) * C::BUF;
+  // One key tile: computes from ks while the next tile is loaded into nbuf.
+  auto tile = [&](int kt, const uint16_t* __restrict__ ks, uint16_t* __restrict__ nbuf)
+                  __attribute__((always_inline)) {
     const uint16_t* vs = ks + C::K_ELEMS;
     const bool more = kt + 1 < kt1;
     if constexpr (kDirect) {
-      if (more) dstage.issue(a, bh, kt + 1, wave, lane, smem + ((kt + 1) & 1) * C::BUF);
+      if (more) dstage.issue(a, bh, kt + 1, wave, lane, nbuf);
     } else {
       if (more) stage.load(a, bh, kt + 1, tid);
     }
@@ -427,9 +456,15 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     if constexpr (kDirect) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of tile kt+1 landed
     } else {
-      if (more) stage.store(smem + ((kt + 1) & 1) * C::BUF, tid);
+      if (more) stage.store(nbuf, tid);
     }
     __syncthreads();
+  };
+
+  // Tile kt0 + 2i lives in smem0, kt0 + 2i + 1 in smem1.
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const bool odd = (kt - kt0) & 1;
+    tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1);
   }
 
   const float l_tot = l_run + lane_xor32(l_run, g);
