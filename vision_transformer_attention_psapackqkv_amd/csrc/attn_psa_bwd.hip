@@ -166,9 +166,13 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
   constexpr int NDK = DP / 32, NDV = DV / 32;
   constexpr int Q_EL = DP * kTN, DO_EL = DV * kTN;
   constexpr int BUF = Q_EL + DO_EL + 2 * kTN * 2;   // + LSE*log2(e) and Delta (floats)
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
+  // Two tile buffers as two objects reached through restrict pointers, so the
+  // LDS reads of one tile need not wait for the direct loads into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t smem0[BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t smem1[BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, t16 = (lane >> 4) & 1;
   const int N = a.N;
   int bh, kt;
@@ -180,8 +184,8 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
 
   if constexpr (DP > KD) {   // Q tile rows KD..DP-1 stay zero
     for (int e = tid; e < (DP - KD) * kTN; e += kThreadsBwd) {
-      smem[KD * kTN + e] = 0;
-      smem[BUF + KD * kTN + e] = 0;
+      smem0[KD * kTN + e] = 0;
+      smem1[KD * kTN + e] = 0;
     }
   }
 
@@ -237,16 +241,17 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
   };
 
   const int n_tiles = (N + kTN - 1) / kTN;
-  issue(0, smem);
-  finish(smem);
+  issue(0, smem0);
+  finish(smem0);
   __syncthreads();
 
-  for (int qt = 0; qt < n_tiles; ++qt) {
-    const uint16_t* qs = smem + (qt & 1) * BUF;
+  // One query tile, read from qs while the next one is loaded into nbuf.
+  auto tile = [&](int qt, const uint16_t* __restrict__ qs, uint16_t* __restrict__ nbuf)
+                  __attribute__((always_inline)) {
     const uint16_t* gs = qs + Q_EL;
     const float* fl = reinterpret_cast<const float*>(gs + DO_EL);
     const bool more = qt + 1 < n_tiles;
-    if (more) issue(qt + 1, smem + ((qt + 1) & 1) * BUF);
+    if (more) issue(qt + 1, nbuf);
 
 #pragma unroll 1
     for (int qb = 0; qb < kTN / 32; ++qb) {
@@ -296,8 +301,12 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
           dk[b] = mfma32x32x16(tile_read8(qs, b * 32 + l32, 4 * qb + 2 * s + g), sb[s], dk[b]);
       }
     }
-    if (more) finish(smem + ((qt + 1) & 1) * BUF);
+    if (more) finish(nbuf);
     __syncthreads();
+  };
+  for (int qt = 0; qt < n_tiles; ++qt) {   // tile t lives in smem0 for even t, smem1 for odd
+    const bool odd = qt & 1;
+    tile(qt, odd ? smem1 : smem0, odd ? smem0 : smem1);
   }
 
   if (!k_ok) return;
@@ -331,9 +340,13 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
   constexpr int NDS = KD / 16, NVS = DV / 16, NDB = DP / 32;
   constexpr int K_EL = DP * kTN, V_EL = DV * kTN;
   constexpr int BUF = K_EL + V_EL;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
+  // Two tile buffers as two objects reached through restrict pointers, so the
+  // LDS reads of one tile need not wait for the direct loads into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t smem0[BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t smem1[BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, t16 = (lane >> 4) & 1;
   const int N = a.N;
   int bh, qt;
@@ -345,8 +358,8 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
 
   if constexpr (DP > KD) {   // K tile rows KD..DP-1 stay zero
     for (int e = tid; e < (DP - KD) * kTN; e += kThreadsBwd) {
-      smem[KD * kTN + e] = 0;
-      smem[BUF + KD * kTN + e] = 0;
+      smem0[KD * kTN + e] = 0;
+      smem1[KD * kTN + e] = 0;
     }
   }
 
@@ -387,15 +400,16 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
   };
 
   const int n_tiles = (N + kTN - 1) / kTN;
-  issue(0, smem);
-  finish(smem);
+  issue(0, smem0);
+  finish(smem0);
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const uint16_t* ks = smem + (kt & 1) * BUF;
+  // One key tile, read from ks while the next one is loaded into nbuf.
+  auto tile = [&](int kt, const uint16_t* __restrict__ ks, uint16_t* __restrict__ nbuf)
+                  __attribute__((always_inline)) {
     const uint16_t* vs_ = ks + K_EL;
     const bool more = kt + 1 < n_tiles;
-    if (more) issue(kt + 1, smem + ((kt + 1) & 1) * BUF);
+    if (more) issue(kt + 1, nbuf);
 
     bf16x8 sb[kTN / 16];   // dS^T, 16 keys per step
 #pragma unroll
@@ -433,8 +447,12 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
 #pragma unroll
       for (int b = 0; b < NDB; ++b) dq[b] = mfma32x32x16(tile_read8(ks, b * 32 + l32, 2 * s + g), sb[s], dq[b]);
 
-    if (more) finish(smem + ((kt + 1) & 1) * BUF);
+    if (more) finish(nbuf);
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_tiles; ++kt) {   // tile t lives in smem0 for even t, smem1 for odd
+    const bool odd = kt & 1;
+    tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1);
   }
 
   if (!q_ok) return;
