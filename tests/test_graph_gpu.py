@@ -1,0 +1,75 @@
+"""The forward and the PSA backward captured in a HIP graph (torch.cuda.CUDAGraph over the
+library's C calls on the capturing stream): every replay equals the eager launch. The
+launches allocate nothing and enqueue no memset, so they can be captured as they are."""
+import pytest
+import torch
+
+import psa_inputs as I
+import vision_transformer_attention_psapackqkv_amd as psa
+from tests.gpu_helpers import announce, device
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays_match(graph, outputs, eager, churn):
+    for i in range(3):
+        for t in outputs:
+            t.zero_()
+        churn()                       # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outputs, eager):
+            assert torch.equal(got, want), f"replay {i} differs from the eager launch"
+
+
+def test_psa_attention_fwd_in_a_graph():
+    dev = device()
+    B, h, KD, H, W = 4, 8, 64, 80, 80     # the benchmark map: its grid splits the last round
+    announce("psa_attention_fwd graph capture")
+    x = I.make_qkv(B, h, KD, H, W, seed=41).to(dev)
+    ws = torch.empty(psa.psa_attention_fwd_workspace_bytes(B, h, KD, H, W), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 2 * h * KD, H, W), dtype=x.dtype, device=dev)
+    vres, lse = torch.empty_like(out), torch.empty((B * h, H * W), dtype=torch.float32, device=dev)
+    e_out, e_v, e_lse = psa.psa_attention_fwd(x, h, KD, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):        # warm-up on the side stream before capture
+        psa.psa_attention_fwd(x, h, KD, out=out, v_out=vres, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        psa.psa_attention_fwd(x, h, KD, out=out, v_out=vres, lse=lse, workspace=ws)
+    y = torch.randn(1 << 20, device=dev)
+
+    def churn():
+        psa.psa_pack_qkv(x, h, KD)
+        y.mul_(1.5)
+    _replays_match(g, [out, vres, lse], [e_out, e_v, e_lse], churn)
+
+
+def test_psa_attention_bwd_in_a_graph():
+    dev = device()
+    B, h, KD, H, W = 2, 4, 32, 24, 24
+    announce("psa_attention_bwd graph capture")
+    x = I.make_qkv(B, h, KD, H, W, seed=42).to(dev)
+    out, _, lse = psa.psa_attention_fwd(x, h, KD, want_v=False)
+    g_out = torch.randn(out.shape, device=dev).to(out.dtype)
+    g_v = torch.randn(out.shape, device=dev).to(out.dtype)
+    ws = torch.empty((psa.load_library().psa_attention_bwd_workspace_bytes(B, h, H, W) // 4,),
+                     dtype=torch.float32, device=dev)
+    dqkv = torch.empty_like(x)
+    eager = psa.psa_attention_bwd(x, out, lse, g_out, h, KD, dv=g_v, workspace=ws).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        psa.psa_attention_bwd(x, out, lse, g_out, h, KD, dv=g_v, dqkv=dqkv, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        psa.psa_attention_bwd(x, out, lse, g_out, h, KD, dv=g_v, dqkv=dqkv, workspace=ws)
+    _replays_match(g, [dqkv], [eager], lambda: psa.psa_attention_fwd(x, h, KD, want_v=False))
