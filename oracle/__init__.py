@@ -1,4 +1,5 @@
-"""CPU oracle for the PSA attention path (test infrastructure only; see psa_oracle)."""
+"""CPU oracle for the PSA attention path (psa_oracle) and the detect-decode / CIoU-loss kernels
+(yolo_oracle). Test infrastructure only."""
 from .psa_oracle import (  # noqa: F401
     attention,
     attention_bwd,
@@ -11,3 +12,4 @@ from .psa_oracle import (  # noqa: F401
     split_attn,
     unpack_qkv,
 )
+from .yolo_oracle import ciou_backward, ciou_forward, detect_decode  # noqa: F401,E402
