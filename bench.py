@@ -10,8 +10,9 @@ throughput in TFLOP/s, counting the algorithmic 6*BH*N^2*KEY_DIM flops
 Also measured and reported in the same JSON line: the unfused chain (pack,
 FA2 x2, merge, extract), the layout kernels' GB/s against HBM peak (input and
 output buffers rotated over 4 sets larger than the 256 MB Infinity Cache), the
-40x40 forward, the FA2 backward workload and the PSA backward on the 40x40 map. The CPU oracle is timed on a
-bounded sample of the same workload as a reported baseline.
+40x40 forward, the FA2 backward workload, the PSA backward on the 40x40 map, and
+detect-decode and the CIoU loss forward/backward on a batch of 64 images of 640x640 (GB/s against
+HBM peak). The CPU oracle is timed on a bounded sample of the same workload as a reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -48,6 +49,8 @@ def parse_args():
                     help="only run pack, merge and extract a few times (for profiler runs)")
     ap.add_argument("--psa-bwd-only", action="store_true",
                     help="time only the PSA backward on the 40x40 map (for profiling)")
+    ap.add_argument("--yolo-only", action="store_true",
+                    help="time only detect-decode and the CIoU loss kernels (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy 3 times (HBM counter calibration)")
     return ap.parse_args()
@@ -145,6 +148,9 @@ def main():
         return
     if args.psa_bwd_only:
         print(json.dumps({"psa_bwd_40x40": psa_bwd_component(torch, psa, I, dev, args.steps, args.warmup)}))
+        return
+    if args.yolo_only:
+        print(json.dumps(yolo_components(torch, psa, dev, args.steps, args.warmup)))
         return
     w = I.WORKLOADS[WORKLOAD]
     qkv_cpu = I.make_workload_qkv(w)
@@ -289,7 +295,74 @@ def components(torch, psa, I, w, qkv, args):
                              "flops": "10*BH*N^2*D"}
     del q, k, v, do, o, lse_b, ws
     comp["psa_bwd_40x40"] = psa_bwd_component(torch, psa, I, dev, steps, warm)
+    comp.update(yolo_components(torch, psa, dev, steps, warm))
     return comp
+
+
+def time_graph(fns, steps, warm, torch):
+    """Average duration (ms) of one of `fns`, all captured back to back in one HIP graph
+    (so that host launch cost does not pace the GPU), over `steps` replays."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / (steps * len(fns))
+
+
+def yolo_components(torch, psa, dev, steps, warm):
+    """Detect-decode and the CIoU loss forward/backward on a batch of 64 images of 640x640
+    (8400 anchors each), HBM-bound: GB/s of algorithmic bytes against the HBM peak. Each
+    kernel cycles over enough buffer sets (> 256 MB in all) that its data come from HBM."""
+    import yolo_inputs as yi
+    B, A = 64, 8400
+    N = B * A
+    res = {}
+    ax, ay, st = (t.to(dev) for t in yi.anchor_grid())
+    for name, dtype, elt in (("detect_decode_f32_b64", torch.float32, 4),
+                             ("detect_decode_bf16_b64", torch.bfloat16, 2)):
+        per = 2 * B * 4 * A * elt
+        sets = -(-300_000_000 // per)
+        ins = [yi.ltrb_boxes(B, A, dtype=dtype, seed=i).to(dev) for i in range(sets)]
+        outs = [torch.empty_like(x) for x in ins]
+        fns = [lambda x=x, o=o: psa.detect_decode(x, ax, ay, st, out=o) for x, o in zip(ins, outs)]
+        avg = time_graph(fns, steps, warm, torch)
+        nbytes = per + 3 * A * 4
+        res[name] = {"avg_ms": round(avg, 6), "bytes": nbytes, "GB/s": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                     "pct_hbm_peak": round(100 * nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+                     "B": B, "A": A, "sets": sets}
+        del ins, outs, fns
+    sets = -(-300_000_000 // (48 * N))
+    data = [tuple(t.to(dev) for t in yi.ciou_boxes(N, seed=i)) for i in range(sets)]
+    saved = [psa.ciou_loss_fwd(p, g) for p, g, _ in data]
+    fwd_out = [tuple(torch.empty(N, device=dev) for _ in range(4)) for _ in range(sets)]
+
+    avg = time_graph([lambda i=i: psa.ciou_loss_fwd(data[i][0], data[i][1], out=fwd_out[i])
+                      for i in range(sets)], steps, warm, torch)
+    res["ciou_fwd_n537600"] = {"avg_ms": round(avg, 6), "bytes": 48 * N,
+                               "GB/s": round(48 * N / (avg * 1e-3) / 1e9, 1),
+                               "pct_hbm_peak": round(100 * 48 * N / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+                               "N": N, "sets": sets}
+    dps = [torch.empty((4, N), device=dev) for _ in range(sets)]
+    fns = [lambda i=i: psa.ciou_loss_bwd(data[i][0], data[i][1], saved[i][1], saved[i][2], saved[i][3],
+                                         data[i][2], dpred=dps[i]) for i in range(sets)]
+    avg = time_graph(fns, steps, warm, torch)
+    res["ciou_bwd_n537600"] = {"avg_ms": round(avg, 6), "bytes": 64 * N,
+                               "GB/s": round(64 * N / (avg * 1e-3) / 1e9, 1),
+                               "pct_hbm_peak": round(100 * 64 * N / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+                               "N": N, "sets": sets}
+    return res
 
 
 def psa_bwd_component(torch, psa, I, dev, steps, warm):

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PSA_ABI_VERSION 2
+#define PSA_ABI_VERSION 3
 
 typedef enum psa_dtype {
   PSA_F32 = 0,
@@ -193,6 +193,50 @@ psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const f
 
 /* Bytes of workspace psa_attention_bwd needs: 2 * B*h * H*W floats. 0 if a size is invalid. */
 size_t psa_attention_bwd_workspace_bytes(int B, int heads, int H, int W);
+
+/*
+ * Detect-decode (vision-rs book, "Custom Kernels", section "Detect-decode";
+ * teenygrad book, "Your Kernel as a Graph Op", section "A real one"): raw LTRB
+ * box distances plus a precomputed anchor grid to [cx, cy, w, h] boxes in one
+ * pass. For batch item b and anchor a, with (l, t, r, bt) = boxes[b][0..3][a]
+ * and (ax, ay, s) = (anchor_x[a], anchor_y[a], strides[a]):
+ *   x1 = ax - l, y1 = ay - t, x2 = ax + r, y2 = ay + bt
+ *   out[b][0..3][a] = ((x1 + x2)/2 * s, (y1 + y2)/2 * s, (x2 - x1) * s, (y2 - y1) * s)
+ * boxes: [B, 4, A] in dtype (PSA_F32 or PSA_BF16). out: [B, 4, A], same dtype
+ * (the op keeps the input's shape and type). anchor_x, anchor_y, strides: [A]
+ * float32 each, the anchor centres in grid units and the grid's stride in
+ * pixels. Arithmetic is float32; a bf16 result is rounded once, to nearest
+ * even. B <= 65535, A < 2^31 - 256. out must not overlap any input.
+ */
+psa_status detect_decode(const void* boxes, const float* anchor_x, const float* anchor_y,
+                         const float* strides, void* out, int B, long long A, psa_dtype dtype,
+                         void* stream);
+
+/*
+ * CIoU loss forward (vision-rs book, "Custom Kernels", section "Loss kernels",
+ * ciou): per anchor n, the complete-IoU loss of box pred[.][n] against
+ * target[.][n] (rows cx, cy, w, h) plus the iou, v and alpha its backward
+ * reuses:
+ *   IoU = I / (w h + w_t h_t - I + eps), I the overlap area
+ *   v = 4/pi^2 (atan(w_t / (h_t + eps)) - atan(w / (h + eps)))^2
+ *   alpha = v / (v - IoU + 1 + eps)
+ *   loss = 1 - IoU + rho^2 / (c^2 + eps) + alpha v
+ * with rho the distance of the centres, c the diagonal of the smallest box
+ * enclosing both, eps = 1e-7. pred, target: [4, N] float32. loss, iou, v,
+ * alpha: [N] float32 outputs. Arithmetic is float32. N < 2^31 - 256.
+ */
+psa_status ciou_loss_fwd(const float* pred, const float* target, float* loss, float* iou,
+                         float* v, float* alpha, long long N, void* stream);
+
+/*
+ * CIoU loss backward (same section): dpred[k][n] = dloss[n] * d loss[n] /
+ * d pred[k][n], alpha held constant (no gradient flows through it; targets
+ * get none). iou, v, alpha: the [N] values ciou_loss_fwd saved for the same
+ * pred and target. dloss: [N] float32. dpred: [4, N] float32 output.
+ */
+psa_status ciou_loss_bwd(const float* pred, const float* target, const float* iou,
+                         const float* v, const float* alpha, const float* dloss, float* dpred,
+                         long long N, void* stream);
 
 /* Message of the last error on this thread ("" after a success). */
 const char* psa_last_error(void);

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     assert names == set(_binding.SIGNATURES), names ^ set(_binding.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.psa_abi_version() == 2
+    assert lib.psa_abi_version() == 3
 
 
 def _status(fn, *args):
@@ -189,3 +189,66 @@ def test_psa_attention_bwd_argument_errors():
     p = list(base)
     p[6] = base[5] + 64               # workspace inside dqkv
     assert call(p)[0] == 5
+
+
+def test_detect_decode_argument_errors():
+    base = [0x1000000 * (i + 1) for i in range(5)]   # boxes, anchor_x, anchor_y, strides, out
+
+    def call(ptrs=base, B=2, A=100, dt=0):
+        return _status("detect_decode", *ptrs, B, A, dt, None)
+
+    for i in range(5):
+        p = list(base)
+        p[i] = None
+        st, msg = call(p)
+        assert st == 1 and msg.startswith("detect_decode"), (i, st, msg)
+    assert call(B=0)[0] == 2
+    assert call(A=0)[0] == 2
+    assert call(B=70000)[0] == 2
+    st, msg = call(dt=5)
+    assert st == 3 and "dtype=5" in msg
+    for i in range(5):
+        p = list(base)
+        p[i] += 4
+        assert call(p)[0] == 4, i
+    p = list(base)
+    p[4] = base[0] + 16                   # out inside boxes (2*4*100 floats)
+    st, msg = call(p)
+    assert st == 5 and "out" in msg
+    p = list(base)
+    p[4] = base[3] - 3200 + 16            # out runs into strides
+    assert call(p)[0] == 5
+
+
+def test_ciou_argument_errors():
+    fwd = [0x1000000 * (i + 1) for i in range(6)]   # pred, target, loss, iou, v, alpha
+    bwd = [0x1000000 * (i + 1) for i in range(7)]   # pred, target, iou, v, alpha, dloss, dpred
+
+    def call_f(ptrs=fwd, N=64):
+        return _status("ciou_loss_fwd", *ptrs, N, None)
+
+    def call_b(ptrs=bwd, N=64):
+        return _status("ciou_loss_bwd", *ptrs, N, None)
+
+    for call, base, fn in ((call_f, fwd, "ciou_loss_fwd"), (call_b, bwd, "ciou_loss_bwd")):
+        for i in range(len(base)):
+            p = list(base)
+            p[i] = None
+            st, msg = call(p)
+            assert st == 1 and msg.startswith(fn), (fn, i, st, msg)
+            p = list(base)
+            p[i] += 8
+            assert call(p)[0] == 4, (fn, i)
+        assert call(N=0)[0] == 2
+        assert call(N=-5)[0] == 2
+        assert call(N=1 << 40)[0] == 2
+    p = list(fwd)
+    p[3] = p[2] + 16                      # iou overlaps loss
+    st, msg = call_f(p)
+    assert st == 5 and "iou" in msg and "loss" in msg
+    p = list(fwd)
+    p[5] = p[0] + 512                     # alpha inside pred (4*64 floats)
+    assert call_f(p)[0] == 5
+    p = list(bwd)
+    p[6] = p[5]                           # dpred aliases dloss
+    assert call_b(p)[0] == 5

@@ -9,6 +9,9 @@ from ._binding import (  # noqa: F401
     PSA_BF16,
     PSA_F32,
     PsaError,
+    ciou_loss_bwd,
+    ciou_loss_fwd,
+    detect_decode,
     default_scale,
     fa2_bwd,
     fa2_fwd,

@@ -33,6 +33,9 @@ SIGNATURES = {
     "psa_attention_fwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "psa_attention_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "psa_attention_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "detect_decode": (_I, [_P, _P, _P, _P, _P, _I, ctypes.c_longlong, _I, _P]),
+    "ciou_loss_fwd": (_I, [_P, _P, _P, _P, _P, _P, ctypes.c_longlong, _P]),
+    "ciou_loss_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_longlong, _P]),
     "psa_last_error": (ctypes.c_char_p, []),
     "psa_abi_version": (_I, []),
 }
@@ -248,6 +251,70 @@ def psa_attention_bwd(qkv, out, lse, dout, heads, key_dim, dv=None, scale=None, 
                                  _ptr(dv), _dev(dqkv, "dqkv").data_ptr(), _dev(workspace, "workspace").data_ptr(),
                                  B, heads, key_dim, H, W, s, _dtype_code(qkv), _stream(qkv)))
     return dqkv
+
+
+def _f32(t, name, shape=None):
+    _dev(t, name)
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def detect_decode(boxes, anchor_x, anchor_y, strides, out=None):
+    """LTRB ``boxes [B, 4, A]`` (float32 or bf16) + anchor grid ``[A]`` x3 (float32) ->
+    ``[B, 4, A]`` cx, cy, w, h in the dtype of ``boxes``."""
+    _dev(boxes, "boxes")
+    if boxes.dim() != 3 or boxes.shape[1] != 4:
+        raise ValueError(f"boxes must be [B, 4, A], got {tuple(boxes.shape)}")
+    B, _, A = boxes.shape
+    for t, n in ((anchor_x, "anchor_x"), (anchor_y, "anchor_y"), (strides, "strides")):
+        _f32(t, n, (A,))
+    if out is None:
+        out = torch.empty_like(boxes)
+    elif out.dtype != boxes.dtype or tuple(out.shape) != tuple(boxes.shape):
+        raise ValueError("out must match boxes in shape and dtype")
+    _check(load_library().detect_decode(boxes.data_ptr(), anchor_x.data_ptr(), anchor_y.data_ptr(),
+                                        strides.data_ptr(), _dev(out, "out").data_ptr(), B, A,
+                                        _dtype_code(boxes), _stream(boxes)))
+    return out
+
+
+def ciou_loss_fwd(pred, target, out=None):
+    """``pred, target [4, N]`` float32 cx, cy, w, h -> ``(loss, iou, v, alpha)``, each ``[N]``
+    (written into ``out``, a tuple of four such tensors, if given)."""
+    _f32(pred, "pred")
+    if pred.dim() != 2 or pred.shape[0] != 4:
+        raise ValueError(f"pred must be [4, N], got {tuple(pred.shape)}")
+    N = pred.shape[1]
+    _f32(target, "target", (4, N))
+    if out is None:
+        out = tuple(torch.empty(N, dtype=torch.float32, device=pred.device) for _ in range(4))
+    loss, iou, v, alpha = (_f32(t, n, (N,)) for t, n in zip(out, ("loss", "iou", "v", "alpha")))
+    _check(load_library().ciou_loss_fwd(pred.data_ptr(), target.data_ptr(), loss.data_ptr(),
+                                        iou.data_ptr(), v.data_ptr(), alpha.data_ptr(), N,
+                                        _stream(pred)))
+    return loss, iou, v, alpha
+
+
+def ciou_loss_bwd(pred, target, iou, v, alpha, dloss, dpred=None):
+    """Gradient ``[4, N]`` of ``sum(dloss * loss)`` w.r.t. ``pred`` from the forward's saved
+    ``iou, v, alpha`` (alpha held constant)."""
+    _f32(pred, "pred")
+    if pred.dim() != 2 or pred.shape[0] != 4:
+        raise ValueError(f"pred must be [4, N], got {tuple(pred.shape)}")
+    N = pred.shape[1]
+    _f32(target, "target", (4, N))
+    for t, n in ((iou, "iou"), (v, "v"), (alpha, "alpha"), (dloss, "dloss")):
+        _f32(t, n, (N,))
+    if dpred is None:
+        dpred = torch.empty((4, N), dtype=torch.float32, device=pred.device)
+    _f32(dpred, "dpred", (4, N))
+    _check(load_library().ciou_loss_bwd(pred.data_ptr(), target.data_ptr(), iou.data_ptr(),
+                                        v.data_ptr(), alpha.data_ptr(), dloss.data_ptr(),
+                                        dpred.data_ptr(), N, _stream(pred)))
+    return dpred
 
 
 def psa_abi_version() -> int:

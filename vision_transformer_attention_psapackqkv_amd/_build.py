@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsa.so")
-SOURCES = ["psa_abi.cpp", "layout.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_psa_bwd.hip"]
+SOURCES = ["psa_abi.cpp", "layout.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_psa_bwd.hip",
+           "detect_decode.hip", "ciou_loss.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [

@@ -76,6 +76,19 @@ psa_status check_disjoint(const char* fn, const Range* r, int n) {
   return PSA_OK;
 }
 
+// r[0, n_in) are inputs, r[n_in, n) outputs: inputs may share memory, but
+// every output must be disjoint from every other range.
+psa_status check_outputs_disjoint(const char* fn, const Range* r, int n, int n_in) {
+  for (int i = n_in; i < n; ++i)
+    for (int j = 0; j < n; ++j)
+      if (j != i && overlap(r[i], r[j]))
+        return fail(PSA_ERR_ALIAS, fn, "%s and %s overlap", r[i].name, r[j].name);
+  return PSA_OK;
+}
+
+// Largest element count of the one-lane-per-element launches (below 2^31 work-items).
+constexpr int64_t kMaxLanes = (int64_t(1) << 31) - 256;
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 psa_status launched(const char* fn, hipError_t e) {
@@ -313,6 +326,71 @@ psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const f
   return launched(fn, psa::launch_psa_fused_bwd(qkv_nchw, out_nchw, lse, dout_nchw, dv_nchw,
                                                 dqkv_nchw, workspace, B * heads, key_dim, H * W,
                                                 scale, as_stream(stream)));
+}
+
+psa_status detect_decode(const void* boxes, const float* anchor_x, const float* anchor_y,
+                         const float* strides, void* out, int B, long long A, psa_dtype dtype,
+                         void* stream) {
+  const char* fn = "detect_decode";
+  if (!boxes) return fail(PSA_ERR_NULL, fn, "boxes is NULL");
+  if (!anchor_x) return fail(PSA_ERR_NULL, fn, "anchor_x is NULL");
+  if (!anchor_y) return fail(PSA_ERR_NULL, fn, "anchor_y is NULL");
+  if (!strides) return fail(PSA_ERR_NULL, fn, "strides is NULL");
+  if (!out) return fail(PSA_ERR_NULL, fn, "out is NULL");
+  if (B <= 0 || A <= 0)
+    return fail(PSA_ERR_SHAPE, fn, "dims must be > 0 (B=%d A=%lld)", B, A);
+  // The batch item is the grid's y index; anchor tiles are the x index.
+  // A grid dimension holds fewer than 2^32 work-items, so the anchor count stays below 2^31.
+  if (B > 65535 || A > kMaxLanes || static_cast<int64_t>(B) * 4 * A > (int64_t(1) << 40))
+    return fail(PSA_ERR_SHAPE, fn, "sizes too large (B=%d A=%lld)", B, A);
+  PSA_TRY(check_dtype(fn, dtype));
+  const void* ptrs[5] = {boxes, anchor_x, anchor_y, strides, out};
+  const char* names[5] = {"boxes", "anchor_x", "anchor_y", "strides", "out"};
+  for (int i = 0; i < 5; ++i) PSA_TRY(check_aligned(fn, names[i], ptrs[i]));
+  const int64_t n = static_cast<int64_t>(B) * 4 * A;
+  const Range r[5] = {range("boxes", boxes, n, elt_bytes(dtype)), range("anchor_x", anchor_x, A, 4),
+                      range("anchor_y", anchor_y, A, 4), range("strides", strides, A, 4),
+                      range("out", out, n, elt_bytes(dtype))};
+  PSA_TRY(check_outputs_disjoint(fn, r, 5, 4));
+  return launched(fn, psa::launch_detect_decode(boxes, anchor_x, anchor_y, strides, out, B, A,
+                                                dtype == PSA_BF16, as_stream(stream)));
+}
+
+psa_status ciou_loss_fwd(const float* pred, const float* target, float* loss, float* iou,
+                         float* v, float* alpha, long long N, void* stream) {
+  const char* fn = "ciou_loss_fwd";
+  const void* ptrs[6] = {pred, target, loss, iou, v, alpha};
+  const char* names[6] = {"pred", "target", "loss", "iou", "v", "alpha"};
+  for (int i = 0; i < 6; ++i)
+    if (!ptrs[i]) return fail(PSA_ERR_NULL, fn, "%s is NULL", names[i]);
+  if (N <= 0) return fail(PSA_ERR_SHAPE, fn, "N=%lld must be > 0", N);
+  if (N > kMaxLanes) return fail(PSA_ERR_SHAPE, fn, "N=%lld too large", N);
+  for (int i = 0; i < 6; ++i) PSA_TRY(check_aligned(fn, names[i], ptrs[i]));
+  const Range r[6] = {range("pred", pred, 4 * N, 4), range("target", target, 4 * N, 4),
+                      range("loss", loss, N, 4),     range("iou", iou, N, 4),
+                      range("v", v, N, 4),           range("alpha", alpha, N, 4)};
+  PSA_TRY(check_outputs_disjoint(fn, r, 6, 2));
+  return launched(fn, psa::launch_ciou_fwd(pred, target, loss, iou, v, alpha, N, as_stream(stream)));
+}
+
+psa_status ciou_loss_bwd(const float* pred, const float* target, const float* iou,
+                         const float* v, const float* alpha, const float* dloss, float* dpred,
+                         long long N, void* stream) {
+  const char* fn = "ciou_loss_bwd";
+  const void* ptrs[7] = {pred, target, iou, v, alpha, dloss, dpred};
+  const char* names[7] = {"pred", "target", "iou", "v", "alpha", "dloss", "dpred"};
+  for (int i = 0; i < 7; ++i)
+    if (!ptrs[i]) return fail(PSA_ERR_NULL, fn, "%s is NULL", names[i]);
+  if (N <= 0) return fail(PSA_ERR_SHAPE, fn, "N=%lld must be > 0", N);
+  if (N > kMaxLanes) return fail(PSA_ERR_SHAPE, fn, "N=%lld too large", N);
+  for (int i = 0; i < 7; ++i) PSA_TRY(check_aligned(fn, names[i], ptrs[i]));
+  const Range r[7] = {range("pred", pred, 4 * N, 4), range("target", target, 4 * N, 4),
+                      range("iou", iou, N, 4),         range("v", v, N, 4),
+                      range("alpha", alpha, N, 4),     range("dloss", dloss, N, 4),
+                      range("dpred", dpred, 4 * N, 4)};
+  PSA_TRY(check_outputs_disjoint(fn, r, 7, 6));
+  return launched(fn, psa::launch_ciou_bwd(pred, target, iou, v, alpha, dloss, dpred, N,
+                                           as_stream(stream)));
 }
 
 const char* psa_last_error(void) { return g_last_error.c_str(); }

@@ -43,4 +43,18 @@ hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const voi
                           float* delta, int BH, int n_q, int n_k, int D, float scale, bool bf16,
                           hipStream_t stream);
 
+// Detect-decode: boxes [B, 4, A] LTRB (float32 or bf16) + anchor grid [A] x3 -> out [B, 4, A].
+hipError_t launch_detect_decode(const void* boxes, const float* anchor_x, const float* anchor_y,
+                                const float* strides, void* out, int B, int64_t A, bool bf16,
+                                hipStream_t stream);
+
+// CIoU loss on [4, N] float32 boxes: per-anchor loss, iou, v, alpha.
+hipError_t launch_ciou_fwd(const float* pred, const float* target, float* loss, float* iou,
+                           float* v, float* alpha, int64_t N, hipStream_t stream);
+
+// CIoU backward: dpred [4, N] from the saved iou, v, alpha and dloss [N].
+hipError_t launch_ciou_bwd(const float* pred, const float* target, const float* iou,
+                           const float* v, const float* alpha, const float* dloss, float* dpred,
+                           int64_t N, hipStream_t stream);
+
 }  // namespace psa
