@@ -168,27 +168,34 @@ struct FwdStageDirect {
     }
   }
 
-  // `wave` must be wave-uniform (an SGPR value): block bases are then scalar
-  // and each load is a scalar base plus this lane's precomputed offset.
+  // `wave` must be wave-uniform (an SGPR value). Tiles are fetched with buffer
+  // loads over the batch-head's [4*KD][N] slab (under 2 GB: the launcher
+  // checks): for a whole tile the lane's offset voff[i] is the same for every
+  // tile and the block's (channel, key) origin is a scalar offset, so issuing
+  // costs no vector instructions. The last, partial tile clamps its keys to
+  // real data (their scores are masked later).
   __device__ __forceinline__ void issue(const FwdArgs& a, int bh, int kt, int wave, int lane,
                                         uint16_t* buf) const {
     const int N = a.n_k;
     const int m0 = kt * kBN;
-    const bool last = m0 + kBN > N;   // keys past n_k: clamped to real data, masked later
+    const bool last = m0 + kBN > N;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.k + static_cast<int64_t>(bh) * 4 * KD * N), 0, 4 * KD * N * 2,
+        kBufferWord3);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int b = wave + i * kWaves;
       if (b >= BLOCKS) break;
-      const uint16_t* row0 = a.k + (static_cast<int64_t>(bh) * 4 * KD + chan0(b)) * N;
-      const uint16_t* src;
-      if (!last) {
-        src = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(row0 + m0) + voff[i]);
-      } else {
+      uint32_t vo = voff[i];
+      int so = (chan0(b) * N + m0) * 2;
+      if (last) {
         int m = m0 + chunk(b, lane) * 8;
         m = m < N ? m : N - 8;
-        src = row0 + static_cast<int64_t>(lane >> 3) * N + m;
+        vo = static_cast<uint32_t>((lane >> 3) * N + m) * 2u;
+        so = chan0(b) * N * 2;
       }
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + b * 512), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(buf + b * 512), 16, vo, so, 0, 0);
     }
   }
 };
@@ -760,6 +767,13 @@ constexpr int occ_target() {
   return KD > 64 ? 1 : (kNCHW && kVecN && KD == 64) ? 3 : 2;
 }
 
+// NCHW tiles are staged straight into LDS with buffer loads whose offsets
+// (32-bit) span one batch-head's [4*KD][N] slab: N a multiple of 8 and the
+// slab under 2 GB. Other maps pass through registers.
+bool fused_direct(int KD, int N) {
+  return N % 8 == 0 && static_cast<int64_t>(8) * KD * N < (int64_t(1) << 31);
+}
+
 template <int KD, int DV, bool kNCHW>
 hipError_t run_bf16(FwdArgs a, bool vec_n, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (vec_n)
@@ -796,7 +810,7 @@ size_t fa2_fwd_split_bytes(int BH, int n_q, int n_k, int D, bool bf16) {
 
 size_t psa_fused_split_bytes(int BH, int KD, int N, bool bf16) {
   if (!bf16) return 0;
-  const bool vec_n = (N % 8) == 0;
+  const bool vec_n = fused_direct(KD, N);
   switch (KD) {
     case 16: return split_bytes<16, 32, true>(BH, N, N, vec_n);
     case 32: return split_bytes<32, 64, true>(BH, N, N, vec_n);
@@ -866,7 +880,7 @@ hipError_t launch_psa_fused_fwd(const void* qkv, void* out, void* vres, float* l
   a.n_q = N;
   a.n_k = N;
   a.c = scale * kLog2e;
-  const bool vec_n = (N % 8) == 0;
+  const bool vec_n = fused_direct(KD, N);
   switch (KD) {
     case 16: return run_bf16<16, 32, true>(a, vec_n, ws, ws_bytes, stream);
     case 32: return run_bf16<32, 64, true>(a, vec_n, ws, ws_bytes, stream);

@@ -86,6 +86,10 @@ __device__ __forceinline__ int tr_key_col(int s) { return ((s & 1) << 3) | ((s &
 // instruction reads together on 16 different bank groups.
 __device__ __forceinline__ int tile_chunk_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
 
+// Word 3 of a gfx9 buffer resource for raw (untyped, unswizzled) byte-offset
+// loads: data format 32 so the hardware does not treat the buffer as invalid.
+constexpr int kBufferWord3 = 0x00020000;
+
 template <typename T>
 __device__ __forceinline__ T ldg_nt(const T* p) { return __builtin_nontemporal_load(p); }
 template <typename T>
