@@ -91,22 +91,33 @@ __device__ __forceinline__ bf16x8 tile_read8(const uint16_t* tile, int row, int 
 // Rows [0, R) x pixels [m0, m0 + 64) of an NCHW slab (row r at src + r*N) into a
 // swizzled LDS tile, straight from global memory: wave instruction b fills the
 // 1 KB of rows 8b .. 8b+7, lane i the i-th 16-byte chunk, fetching the pixel
-// chunk the swizzle puts there. Pixels past N repeat real data (the kernels
-// give them zero weight). Needs N a multiple of 8.
+// chunk the swizzle puts there. Buffer loads over the R x N slab (under 2 GB:
+// the launcher checks): the lane's offset inside its block does not depend on
+// m0, and the block's origin is a scalar offset. Pixels past N repeat real
+// data (the kernels give them zero weight). Needs N a multiple of 8.
 template <int R>
 __device__ __forceinline__ void stage_direct(const uint16_t* src, int N, int m0, int wave, int lane,
                                              uint16_t* dst) {
   constexpr int BLOCKS = R / 8;
   static_assert(R % 8 == 0, "whole 1 KB blocks");
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, R * N * 2, kBufferWord3);
+  const bool last = m0 + kTN > N;
 #pragma unroll
   for (int i = 0; i < (BLOCKS + kWavesBwd - 1) / kWavesBwd; ++i) {
     const int b = wave + i * kWavesBwd;
     if (b >= BLOCKS) break;
-    const int row = b * 8 + (lane >> 3);
-    int m = m0 + tile_chunk_pos(row, lane & 7) * 8;
-    m = m < N ? m : N - 8;
-    __builtin_amdgcn_global_load_lds(src + static_cast<int64_t>(row) * N + m,
-                                     (__attribute__((address_space(3))) void*)(dst + b * 512), 16, 0, 0);
+    const int r = lane >> 3;
+    const int pos = tile_chunk_pos(b * 8 + r, lane & 7) * 8;
+    uint32_t vo = static_cast<uint32_t>(r * N + pos) * 2u;
+    int so = (b * 8 * N + m0) * 2;
+    if (last) {
+      const int m = m0 + pos < N ? m0 + pos : N - 8;
+      vo = static_cast<uint32_t>(r * N + m) * 2u;
+      so = b * 8 * N * 2;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(dst + b * 512), 16, vo, so, 0, 0);
   }
 }
 
@@ -479,7 +490,8 @@ hipError_t run_psa_bwd(PsaBwdArgs a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   a.tiles = (a.N + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
   const dim3 grid(static_cast<unsigned>(a.BH) * a.tiles);
-  const bool vec_n = a.N % 8 == 0;
+  // Direct staging addresses one batch-head's [4*KD][N] slab with 32-bit offsets.
+  const bool vec_n = a.N % 8 == 0 && static_cast<int64_t>(8) * KD * a.N < (int64_t(1) << 31);
   if (vec_n)
     psa_bwd_dkdv<KD, true, kOccDkdv><<<grid, kThreadsBwd, 0, stream>>>(a);
   else   // the register-staged tiles need more registers
