@@ -12,8 +12,8 @@
 // queries and walks all keys in tiles of 64, staged in LDS in the tensors' own
 // layout and double-buffered (the next tile's loads are in flight while the
 // current tile is computed). NCHW tiles with N a multiple of 8 go from global
-// memory straight into LDS (global_load_lds_dwordx4, no registers on the way);
-// the others pass through registers.
+// memory straight into LDS (buffer loads with an LDS destination, no registers
+// on the way); the others pass through registers.
 //
 // Tail split: a grid rarely fills the chip's workgroup slots a whole number of
 // times, and the last partial round would run on a few CUs while the rest idle.
@@ -137,7 +137,7 @@ constexpr int kMaxSplits = 6;
 constexpr int kSplitMinTiles = 16;
 
 // Direct global -> LDS staging of one NCHW key tile (N a multiple of 8): each
-// wave instruction (global_load_lds_dwordx4) fills 64 consecutive 16-byte LDS
+// wave instruction (buffer_load_dwordx4 ... lds) fills 64 consecutive 16-byte LDS
 // chunks, lane i the i-th; lanes pick which global chunk to fetch, which is
 // how the V swizzle is applied. No registers and no LDS write instructions;
 // the wave waits with vmcnt before the barrier that publishes the tile.

@@ -32,7 +32,7 @@
 // the accumulator a lane holds is directly the B operand of the last product.
 // LDS tiles are unpadded rows of 64 pixels with XOR-swizzled 16-byte chunks
 // (tile_chunk_pos), read both ways; they are filled straight from global memory
-// (global_load_lds_dwordx4) when N is a multiple of 8, through registers
+// (buffer loads with an LDS destination) when N is a multiple of 8, through registers
 // otherwise. Scores use base 2: P = 2^(S * s*log2(e) - LSE*log2(e)).
 #include <math.h>
 
