@@ -73,3 +73,38 @@ def test_psa_attention_bwd_in_a_graph():
     with torch.cuda.graph(g):
         psa.psa_attention_bwd(x, out, lse, g_out, h, KD, dv=g_v, dqkv=dqkv, workspace=ws)
     _replays_match(g, [dqkv], [eager], lambda: psa.psa_attention_fwd(x, h, KD, want_v=False))
+
+
+def test_detect_decode_and_ciou_in_a_graph():
+    """Detect-decode (both dtypes) and the CIoU forward and backward in one captured graph."""
+    import yolo_inputs as yi
+    dev = device()
+    announce("detect_decode + ciou graph capture")
+    ax, ay, st = (t.to(dev) for t in yi.anchor_grid())
+    boxes = {dt: yi.ltrb_boxes(8, 8400, dtype=dt, seed=43).to(dev) for dt in (torch.float32, torch.bfloat16)}
+    dec = {dt: torch.empty_like(b) for dt, b in boxes.items()}
+    N = 8 * 8400 + 3                  # ragged: the one-anchor-per-lane kernels
+    p, t, dl = (x.to(dev) for x in yi.ciou_boxes(N, seed=44))
+    fwd = tuple(torch.empty(N, device=dev) for _ in range(4))
+    dp = torch.empty((4, N), device=dev)
+    eager = [psa.detect_decode(b, ax, ay, st) for b in boxes.values()]
+    e_fwd = psa.ciou_loss_fwd(p, t)
+    eager += list(e_fwd) + [psa.ciou_loss_bwd(p, t, e_fwd[1], e_fwd[2], e_fwd[3], dl)]
+
+    def launches():
+        for dt, b in boxes.items():
+            psa.detect_decode(b, ax, ay, st, out=dec[dt])
+        psa.ciou_loss_fwd(p, t, out=fwd)
+        psa.ciou_loss_bwd(p, t, fwd[1], fwd[2], fwd[3], dl, dpred=dp)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launches()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launches()
+    y = torch.randn(1 << 20, device=dev)
+    _replays_match(g, list(dec.values()) + list(fwd) + [dp], eager, lambda: y.mul_(1.5))

@@ -296,58 +296,39 @@ template <int D, int kWaves>
 struct DqTile {
   static constexpr int NT = kWaves * 64;
   static constexpr int BN = 64;                    // keys per tile
-  static constexpr int DP = D < 32 ? 32 : D;
+  static constexpr int DP = D < 32 ? 32 : D;       // dQ rows in whole 32-row blocks
   static constexpr int RSTR = D + kPad;
-  static constexpr int TSTR = BN + kPad;
   static constexpr int R_ELEMS = BN * RSTR;
-  static constexpr int T_ELEMS = DP * TSTR;
-  static constexpr int OFF_K = 0, OFF_V = R_ELEMS, OFF_KT = 2 * R_ELEMS;
-  static constexpr int BUF = 2 * R_ELEMS + T_ELEMS;
-  static constexpr int KBLOCKS = (BN / 8) * (D / 8);   // 8x8 blocks of K (rows + transposed)
-  static constexpr int VCHUNKS = BN * D / 8;           // 16-byte pieces of V rows
-  static constexpr int V_PER = (VCHUNKS + NT - 1) / NT;
-  static_assert(KBLOCKS <= NT, "one K block per thread");
+  static constexpr int OFF_K = 0, OFF_V = R_ELEMS;
+  static constexpr int BUF = 2 * R_ELEMS;
+  static constexpr int CHUNKS = BN * D / 8;        // 16-byte pieces of the K (and of the V) rows
+  static constexpr int PER = (CHUNKS + NT - 1) / NT;
 
-  u32x4 kr[8];
-  u32x4 vr[V_PER];
+  u32x4 kr[PER];
+  u32x4 vr[PER];
 
   __device__ __forceinline__ void load(const BwdArgs& a, int bh, int kt, int tid) {
     const int m0 = kt * BN;
-    if (tid < KBLOCKS) {
-      const int mb = tid / (D / 8), db = tid % (D / 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = m0 + mb * 8 + i;
-        kr[i] = (m < a.n_k) ? load16(a.k + (static_cast<int64_t>(bh) * a.n_k + m) * D + db * 8) : zero4();
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
-      if (c < VCHUNKS) {
+      if (c < CHUNKS) {
         const int r = c / (D / 8), cb = c % (D / 8);
         const int m = m0 + r;
-        vr[i] = (m < a.n_k) ? load16(a.v + (static_cast<int64_t>(bh) * a.n_k + m) * D + cb * 8) : zero4();
+        const int64_t off = (static_cast<int64_t>(bh) * a.n_k + m) * D + cb * 8;
+        kr[i] = (m < a.n_k) ? load16(a.k + off) : zero4();
+        vr[i] = (m < a.n_k) ? load16(a.v + off) : zero4();
       }
     }
   }
 
   __device__ __forceinline__ void store(uint16_t* buf, int tid) const {
-    if (tid < KBLOCKS) {
-      const int mb = tid / (D / 8), db = tid % (D / 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(buf + OFF_K + (mb * 8 + i) * RSTR + db * 8) = kr[i];
-      u32x4 t[8];
-      transpose8x8(kr, t);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) store_t8(buf + OFF_KT + (db * 8 + c) * TSTR, mb, t[c]);
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
-      if (c < VCHUNKS) {
+      if (c < CHUNKS) {
         const int r = c / (D / 8), cb = c % (D / 8);
+        *reinterpret_cast<u32x4*>(buf + OFF_K + r * RSTR + cb * 8) = kr[i];
         *reinterpret_cast<u32x4*>(buf + OFF_V + r * RSTR + cb * 8) = vr[i];
       }
     }
@@ -364,17 +345,11 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dq_bf16(BwdA
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Tile::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int i16 = lane & 15, t16 = (lane >> 4) & 1;
   int bh, qt;
   block_of(a.BH * a.tiles, a.tiles, bh, qt);
   const int q = qt * BM + wave * 32 + l32;
   const bool q_ok = q < a.n_q;
-
-  if constexpr (Tile::DP > D) {
-    for (int e = tid; e < (Tile::DP - D) * Tile::TSTR; e += Tile::NT) {
-      smem[Tile::OFF_KT + D * Tile::TSTR + e] = 0;
-      smem[Tile::BUF + Tile::OFF_KT + D * Tile::TSTR + e] = 0;
-    }
-  }
 
   bf16x8 qop[NDS], gop[NDS];
 #pragma unroll
@@ -406,7 +381,9 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dq_bf16(BwdA
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
       // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T (its accumulator starts at
-      // -Delta, so it ends as dP^T - Delta).
+      // -Delta, so it ends as dP^T - Delta). Row rho of the A operands is key
+      // key_of_row(rho), so element r of lane group g holds key 16*(r/8) + 8g + r%8
+      // of the block: the dS values come out as B operands of the dQ product.
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -415,7 +392,7 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dq_bf16(BwdA
       }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        const int off = (kb * 32 + l32) * Tile::RSTR + ds * 16 + g * 8;
+        const int off = (kb * 32 + key_of_row(l32)) * Tile::RSTR + ds * 16 + g * 8;
         sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_K + off), qop[ds], sacc);
         pacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_V + off), gop[ds], pacc);
       }
@@ -423,7 +400,7 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dq_bf16(BwdA
       if ((kt + 1) * BN > a.n_k) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kt * BN + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= a.n_k) sacc[r] = -INFINITY;
+          if (kt * BN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7) >= a.n_k) sacc[r] = -INFINITY;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -431,13 +408,21 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dq_bf16(BwdA
         sb[kb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p * pacc[r]);
       }
     }
-    // dQ^T += K^T dS^T (reduction over the tile's keys).
+    // dQ^T += K^T dS^T (reduction over the tile's keys); K^T comes from the K rows
+    // through transposed LDS reads. With D = 16 the second 16-row half of the
+    // block reads past the row (finite data) and is zeroed: those dQ rows are
+    // never stored.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int s = 0; s < BN / 16; ++s) {
-        const int off = (db * 32 + l32) * Tile::TSTR + s * 16 + g * 8;
-        dq_acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_KT + off), sb[s], dq_acc[db]);
+        bf16x8 kop = lds_read_tr8(buf + Tile::OFF_K + (s * 16 + 8 * g + (i16 >> 2)) * Tile::RSTR + db * 32 +
+                                      16 * t16 + 4 * (i16 & 3),
+                                  Tile::RSTR);
+        if constexpr (Tile::DP > D) {
+          if (db * 32 + l32 >= D) kop = as_bf16x8(zero4());
+        }
+        dq_acc[db] = mfma32x32x16(kop, sb[s], dq_acc[db]);
       }
     if (more) tile.store(smem + ((kt + 1) & 1) * Tile::BUF, tid);
     __syncthreads();
