@@ -10,11 +10,12 @@
 // looping over key tiles). Neither uses atomics.
 //
 // The matrix-core products use v_mfma_f32_32x32x16_bf16 with the operand
-// placement of the forward kernel: a product is arranged so that the
-// accumulator of the first product (the scores) is already the register
-// operand of the next one, and the operand read from LDS with the reduction
-// index contiguous is staged transposed (8x8 register transposes on the way
-// in, rows permuted inside each group of 16 like the forward's V^T).
+// placement of the forward kernel: the rows of the first products' LDS
+// operands are permuted (key_of_row) so that their accumulators (the scores,
+// P and dS) are already the register operands of the next products, and the
+// LDS operands of those products, whose reduction index runs down the staged
+// rows, are read from the same row tiles with transposed LDS reads
+// (ds_read_b64_tr_b16). Tiles are staged once, as plain padded rows.
 #include <math.h>
 
 #include "psa_device.hpp"
@@ -42,27 +43,6 @@ struct BwdArgs {
   float c;              // scale * log2(e)
 };
 
-
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = in[2 * w][c >> 1];
-      const uint32_t hi = in[2 * w + 1][c >> 1];
-      out[c][w] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-  }
-}
-
-// 8 consecutive rows (8*mb .. 8*mb+7 of a tile) of one transposed row, at the
-// permuted positions the MFMA B-operand order needs: inside each group of 16,
-// index kappa goes to 8*((kappa/4)%2) + 4*(kappa/8) + kappa%4.
-__device__ __forceinline__ void store_t8(uint16_t* row, int mb, u32x4 v) {
-  const int base = (mb >> 1) * 16 + (mb & 1) * 4;
-  *reinterpret_cast<u32x2*>(row + base) = u32x2{v[0], v[1]};
-  *reinterpret_cast<u32x2*>(row + base + 8) = u32x2{v[2], v[3]};
-}
 
 __device__ __forceinline__ void block_of(int total, int tiles, int& bh, int& t) {
   const int i = blockIdx.x;
@@ -107,32 +87,30 @@ template <int D, int kWaves>
 struct DkdvTile {
   static constexpr int NT = kWaves * 64;
   static constexpr int BQ = 64;                    // queries per tile
-  static constexpr int DP = D < 32 ? 32 : D;       // transposed rows, padded to one MFMA block
+  static constexpr int DP = D < 32 ? 32 : D;       // dK/dV rows in whole 32-row blocks
   static constexpr int RSTR = D + kPad;            // [q][d] tiles
-  static constexpr int TSTR = BQ + kPad;           // [d][q] tiles
   static constexpr int R_ELEMS = BQ * RSTR;
-  static constexpr int T_ELEMS = DP * TSTR;
   // Layout of one buffer (bf16 elements, then floats).
-  static constexpr int OFF_Q = 0, OFF_DO = R_ELEMS, OFF_QT = 2 * R_ELEMS, OFF_DOT = 2 * R_ELEMS + T_ELEMS;
-  static constexpr int H_ELEMS = 2 * R_ELEMS + 2 * T_ELEMS;   // bf16 elements (even count)
+  static constexpr int OFF_Q = 0, OFF_DO = R_ELEMS;
+  static constexpr int H_ELEMS = 2 * R_ELEMS;      // bf16 elements (even count)
   static constexpr int BUF_BYTES = H_ELEMS * 2 + 2 * BQ * 4;
-  static constexpr int BLOCKS = 2 * (BQ / 8) * (D / 8);      // 8x8 blocks of Q and dO
-  static_assert(BLOCKS <= NT, "one 8x8 block per thread");
+  static constexpr int CHUNKS = BQ * D / 8;        // 16-byte pieces of the Q (and of the dO) rows
+  static constexpr int PER = (CHUNKS + NT - 1) / NT;
 
-  u32x4 r[8];
+  u32x4 qr[PER], gr[PER];
   float l2, dl;
 
   __device__ __forceinline__ void load(const BwdArgs& a, int bh, int qt, int tid) {
     const int q0 = qt * BQ;
-    if (tid < BLOCKS) {
-      const int which = tid / (BLOCKS / 2);          // 0: Q, 1: dO
-      const int b = tid % (BLOCKS / 2);
-      const int mb = b / (D / 8), db = b % (D / 8);
-      const uint16_t* src = which ? a.dout : a.q;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int qq = q0 + mb * 8 + i;
-        r[i] = (qq < a.n_q) ? load16(src + (static_cast<int64_t>(bh) * a.n_q + qq) * D + db * 8) : zero4();
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * NT;
+      if (c < CHUNKS) {
+        const int r = c / (D / 8), cb = c % (D / 8);
+        const int qq = q0 + r;
+        const int64_t off = (static_cast<int64_t>(bh) * a.n_q + qq) * D + cb * 8;
+        qr[i] = (qq < a.n_q) ? load16(a.q + off) : zero4();
+        gr[i] = (qq < a.n_q) ? load16(a.dout + off) : zero4();
       }
     }
     if (tid < BQ) {
@@ -147,18 +125,14 @@ struct DkdvTile {
   __device__ __forceinline__ void store(char* buf, int tid) const {
     uint16_t* h = reinterpret_cast<uint16_t*>(buf);
     float* f = reinterpret_cast<float*>(buf + H_ELEMS * 2);
-    if (tid < BLOCKS) {
-      const int which = tid / (BLOCKS / 2);
-      const int b = tid % (BLOCKS / 2);
-      const int mb = b / (D / 8), db = b % (D / 8);
-      uint16_t* rows = h + (which ? OFF_DO : OFF_Q);
-      uint16_t* tr = h + (which ? OFF_DOT : OFF_QT);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(rows + (mb * 8 + i) * RSTR + db * 8) = r[i];
-      u32x4 t[8];
-      transpose8x8(r, t);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) store_t8(tr + (db * 8 + c) * TSTR, mb, t[c]);
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * NT;
+      if (c < CHUNKS) {
+        const int r = c / (D / 8), cb = c % (D / 8);
+        *reinterpret_cast<u32x4*>(h + OFF_Q + r * RSTR + cb * 8) = qr[i];
+        *reinterpret_cast<u32x4*>(h + OFF_DO + r * RSTR + cb * 8) = gr[i];
+      }
     }
     if (tid < BQ) {
       f[tid] = l2;
@@ -178,21 +152,11 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dkdv_bf16(Bw
   __shared__ __attribute__((aligned(16))) char smem[2 * Tile::BUF_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int i16 = lane & 15, t16 = (lane >> 4) & 1;
   int bh, kt;
   block_of(a.BH * a.tiles, a.tiles, bh, kt);
   const int key = kt * 32 * kWaves + wave * 32 + l32;
   const bool k_ok = key < a.n_k;
-
-  // Padded transposed rows (D = 16) stay zero.
-  if constexpr (Tile::DP > D) {
-    for (int b = 0; b < 2; ++b) {
-      uint16_t* h = reinterpret_cast<uint16_t*>(smem + b * Tile::BUF_BYTES);
-      for (int e = tid; e < (Tile::DP - D) * Tile::TSTR; e += Tile::NT) {
-        h[Tile::OFF_QT + D * Tile::TSTR + e] = 0;
-        h[Tile::OFF_DOT + D * Tile::TSTR + e] = 0;
-      }
-    }
-  }
 
   // This lane's key and value rows as B operands: K[key][16ds + 8g + j].
   bf16x8 kop[NDS], vop[NDS];
@@ -223,13 +187,15 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dkdv_bf16(Bw
 
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
-      // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries, at the lane's
-      // queries qb*32 + 8*(r/4) + 4g + r%4; dP's accumulator starts at -Delta,
-      // so it ends as dP - Delta.
+      // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries. Row rho of the
+      // A operands is query key_of_row(rho), so element r of lane group g holds
+      // query qb*32 + 16*(r/8) + 8g + r%8 (P and dS come out as B operands over
+      // 8 consecutive queries); dP's accumulator starts at -Delta, so it ends as
+      // dP - Delta.
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(f + BQ + qb * 32 + 8 * r4 + 4 * g);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(f + BQ + qb * 32 + 16 * (r4 >> 1) + 8 * g + 4 * (r4 & 1));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sacc[4 * r4 + e] = 0.0f;
@@ -238,7 +204,7 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dkdv_bf16(Bw
       }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        const int off = (qb * 32 + l32) * Tile::RSTR + ds * 16 + g * 8;
+        const int off = (qb * 32 + key_of_row(l32)) * Tile::RSTR + ds * 16 + g * 8;
         sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_Q + off), kop[ds], sacc);
         pacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_DO + off), vop[ds], pacc);
       }
@@ -246,7 +212,7 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dkdv_bf16(Bw
       bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(f + qb * 32 + 8 * r4 + 4 * g);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(f + qb * 32 + 16 * (r4 >> 1) + 8 * g + 4 * (r4 & 1));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
@@ -255,14 +221,22 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dkdv_bf16(Bw
           sb[r >> 3][r & 7] = static_cast<__bf16>(p * pacc[r]);
         }
       }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the 32 queries, 2 steps of 16).
+      // dV^T += dO^T P,  dK^T += Q^T dS  (reduction over the 32 queries, 2 steps of
+      // 16). dO^T and Q^T come from the row tiles through transposed LDS reads; with
+      // D = 16 the second 16-row half of the block reads past the row (finite data)
+      // and is zeroed: those rows are never stored.
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const int off = (db * 32 + l32) * Tile::TSTR + (qb * 2 + s) * 16 + g * 8;
-          dv_acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_DOT + off), pb[s], dv_acc[db]);
-          dk_acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(h + Tile::OFF_QT + off), sb[s], dk_acc[db]);
+          const int off = ((qb * 2 + s) * 16 + 8 * g + (i16 >> 2)) * Tile::RSTR + db * 32 + 16 * t16 + 4 * (i16 & 3);
+          bf16x8 gt = lds_read_tr8(h + Tile::OFF_DO + off, Tile::RSTR);
+          bf16x8 qt_op = lds_read_tr8(h + Tile::OFF_Q + off, Tile::RSTR);
+          if constexpr (Tile::DP > D) {
+            if (db * 32 + l32 >= D) gt = qt_op = as_bf16x8(zero4());
+          }
+          dv_acc[db] = mfma32x32x16(gt, pb[s], dv_acc[db]);
+          dk_acc[db] = mfma32x32x16(qt_op, sb[s], dk_acc[db]);
         }
     }
     if (more) tile.store(smem + ((qt + 1) & 1) * Tile::BUF_BYTES, tid);
