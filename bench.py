@@ -47,6 +47,8 @@ def parse_args():
                     help="time only the fused step (for profiler runs)")
     ap.add_argument("--layout-only", action="store_true",
                     help="only run pack, merge and extract a few times (for profiler runs)")
+    ap.add_argument("--fa2-bwd-only", action="store_true",
+                    help="time only the FA2 backward on the 40x40 workload (for profiling)")
     ap.add_argument("--psa-bwd-only", action="store_true",
                     help="time only the PSA backward on the 40x40 map (for profiling)")
     ap.add_argument("--yolo-only", action="store_true",
@@ -145,6 +147,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes_read": src.numel() * 2,
                           "calibration_copy_bytes_written": dst.numel() * 2}))
+        return
+    if args.fa2_bwd_only:
+        print(json.dumps({"fa2_bwd_40x40": fa2_bwd_component(torch, psa, I, dev, args.steps, args.warmup)}))
         return
     if args.psa_bwd_only:
         print(json.dumps({"psa_bwd_40x40": psa_bwd_component(torch, psa, I, dev, args.steps, args.warmup)}))
@@ -283,17 +288,7 @@ def components(torch, psa, I, w, qkv, args):
     comp["fused_fwd_40x40"] = {"avg_ms": round(avg, 5), "TFLOP/s": round(t2, 3),
                                "pct_bf16_mfma_peak": round(100 * t2 / PEAK_BF16_TFLOPS, 2)}
     del q2, o_2, v_2, l_2
-    # The FA2 backward workload (Delta + dK/dV + dQ launches).
-    wb = I.WORKLOADS["fa2_bwd_bf16_40x40"]
-    q, k, v, do = (t.to(dev) for t in I.make_workload_bwd(wb))
-    o, lse_b = psa.fa2_fwd(q, k, v)
-    ws = torch.empty((wb.BH * wb.N,), dtype=torch.float32, device=dev)
-    avg, _, _ = time_events(lambda i: psa.fa2_bwd(q, k, v, o, do, lse_b, workspace=ws), steps, warm, torch)
-    tb = 10.0 * wb.BH * wb.N ** 2 * wb.key_dim / (avg * 1e-3) / 1e12
-    comp["fa2_bwd_40x40"] = {"avg_ms": round(avg, 5), "TFLOP/s": round(tb, 3),
-                             "pct_bf16_mfma_peak": round(100 * tb / PEAK_BF16_TFLOPS, 2),
-                             "flops": "10*BH*N^2*D"}
-    del q, k, v, do, o, lse_b, ws
+    comp["fa2_bwd_40x40"] = fa2_bwd_component(torch, psa, I, dev, steps, warm)
     comp["psa_bwd_40x40"] = psa_bwd_component(torch, psa, I, dev, steps, warm)
     comp.update(yolo_components(torch, psa, dev, steps, warm))
     return comp
@@ -363,6 +358,18 @@ def yolo_components(torch, psa, dev, steps, warm):
                                "pct_hbm_peak": round(100 * 64 * N / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
                                "N": N, "sets": sets}
     return res
+
+
+def fa2_bwd_component(torch, psa, I, dev, steps, warm):
+    """The FA2 backward workload (Delta + dK/dV + dQ launches), O and LSE from fa2_fwd."""
+    wb = I.WORKLOADS["fa2_bwd_bf16_40x40"]
+    q, k, v, do = (t.to(dev) for t in I.make_workload_bwd(wb))
+    o, lse_b = psa.fa2_fwd(q, k, v)
+    ws = torch.empty((wb.BH * wb.N,), dtype=torch.float32, device=dev)
+    avg, _, _ = time_events(lambda i: psa.fa2_bwd(q, k, v, o, do, lse_b, workspace=ws), steps, warm, torch)
+    tb = 10.0 * wb.BH * wb.N ** 2 * wb.key_dim / (avg * 1e-3) / 1e12
+    return {"avg_ms": round(avg, 5), "TFLOP/s": round(tb, 3), "pct_bf16_mfma_peak": round(100 * tb / PEAK_BF16_TFLOPS, 2),
+            "flops": "10*BH*N^2*D"}
 
 
 def psa_bwd_component(torch, psa, I, dev, steps, warm):
