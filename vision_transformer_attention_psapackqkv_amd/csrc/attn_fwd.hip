@@ -45,6 +45,8 @@
 // product and the row sum adds the same rounded values.
 #include <math.h>
 
+#include <type_traits>
+
 #include "psa_device.hpp"
 #include "psa_launch.hpp"
 
@@ -105,6 +107,14 @@ __device__ __forceinline__ float lane_xor32(float x, int g) {
   const u32x2 sw = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane32_swap(
       __builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false));
   return __builtin_bit_cast(float, g ? sw[0] : sw[1]);
+}
+
+// Whether a kernel instance stages its tiles straight into LDS: NCHW tiles
+// with N a multiple of 8, packed tiles with head dim 32..128 (kVecN then means
+// the rows fit the buffer offsets).
+template <int KD, bool kNCHW, bool kVecN>
+constexpr bool direct_staging() {
+  return kVecN && (kNCHW || KD >= 32);
 }
 
 template <int KD, int DV, bool kNCHW, int kWaves, bool kDirect>
@@ -200,6 +210,80 @@ struct FwdStageDirect {
   }
 };
 
+// Position of 16-byte chunk c of row `row` in an unpadded packed tile of D
+// columns (D/8 chunks per row): an XOR swizzle chosen so that neither the
+// K-operand reads (16 bytes per lane, rows in key_of_row order) nor the
+// transposed V-operand reads (8 bytes per lane, rows r and r + 4) of one
+// instruction meet twice on a bank.
+template <int D>
+__device__ __forceinline__ int packed_chunk_pos(int row, int c) {
+  static_assert(D == 32 || D == 64 || D == 128, "packed direct staging");
+  if constexpr (D == 32) return c ^ ((row >> 2) & 3);
+  if constexpr (D == 64)
+    return c ^ (((row >> 1) & 1) | (((row >> 2) & 1) << 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 2));
+  return c ^ ((row & 1) | (((row >> 1) & 1) << 1) | (((row ^ (row >> 2)) & 1) << 2) |
+              ((((row >> 1) ^ (row >> 3)) & 1) << 3));
+}
+
+// Direct global -> LDS staging of one packed key tile ([BH, n, D] K and V,
+// D >= 32): 64 rows of D elements each, unpadded, chunks placed by
+// packed_chunk_pos. Wave instruction b fills one 1 KB block (512 / D rows);
+// lane i fetches the global chunk the swizzle puts at LDS chunk i. Buffer
+// loads over one batch-head's [n_k][D] rows (under 2 GB: the launcher checks):
+// for a whole tile the lane's offset is the same for every tile and the
+// tile's first row is a scalar offset. The last, partial tile repeats row
+// n_k - 1 (its scores are masked).
+template <int KD, int DV, int kWaves>
+struct FwdStagePacked {
+  static_assert(KD == DV, "packed direct staging serves fa2_fwd (value width = head dim)");
+  static constexpr int CPR = KD / 8;                       // chunks per row
+  static constexpr int RPB = 64 / CPR;                     // rows per 1 KB block
+  static constexpr int K_BLOCKS = kBN / RPB;
+  static constexpr int BLOCKS = 2 * K_BLOCKS;              // K blocks, then V blocks
+  static constexpr int PER = (BLOCKS + kWaves - 1) / kWaves;
+
+  __device__ static int row_of(int b, int lane) { return (b % K_BLOCKS) * RPB + lane / CPR; }
+  __device__ static int chunk_of(int b, int lane) {
+    return packed_chunk_pos<KD>(row_of(b, lane), lane % CPR);   // the swizzle is an involution
+  }
+
+  uint32_t voff[PER];   // byte offset of this lane's 16 bytes from the tile's first row
+
+  __device__ __forceinline__ void init(int /*N*/, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int b = wave + i * kWaves;
+      voff[i] = b < BLOCKS ? static_cast<uint32_t>(row_of(b, lane) * KD + chunk_of(b, lane) * 8) * 2u : 0u;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const FwdArgs& a, int bh, int kt, int wave, int lane,
+                                        uint16_t* buf) const {
+    const int n = a.n_k;
+    const int m0 = kt * kBN;
+    const bool last = m0 + kBN > n;
+    const int64_t base = static_cast<int64_t>(bh) * n * KD;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.k + base), 0, n * KD * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.v + base), 0, n * KD * 2, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int b = wave + i * kWaves;
+      if (b >= BLOCKS) break;
+      uint32_t vo = voff[i];
+      if (last) {
+        const int r = row_of(b, lane);
+        const int m = m0 + r < n ? r : n - 1 - m0;
+        vo = static_cast<uint32_t>(m * KD + chunk_of(b, lane) * 8) * 2u;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          b < K_BLOCKS ? rk : rv, (__attribute__((address_space(3))) void*)(buf + b * 512), 16, vo,
+          m0 * KD * 2, 0, 0);
+    }
+  }
+};
+
 // Global -> registers -> LDS staging of one key tile (K and V), 16-byte chunks.
 // Keys past n_k are clamped to real rows (finite data): their scores are
 // masked to -inf, so they contribute nothing. The unaligned NCHW variant
@@ -254,7 +338,7 @@ struct FwdStage {
 // kOcc: waves per SIMD the register allocation must allow.
 template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
 __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
-  constexpr bool kDirect = kNCHW && kVecN;   // direct global -> LDS staging
+  constexpr bool kDirect = direct_staging<KD, kNCHW, kVecN>();
   using C = FwdCfg<KD, DV, kNCHW, kWaves, kDirect>;
   constexpr int NT = C::NT;
   constexpr int BM = C::BM;
@@ -304,7 +388,7 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   const bool q_ok = q_row < a.n_q;
 
   // Packed V with DV = 16: columns 16..31 of every V row stay zero in both buffers.
-  if constexpr (!kNCHW && C::DVP > DV) {
+  if constexpr (!kNCHW && !kDirect && C::DVP > DV) {
     for (int e = tid; e < kBN * (C::DVP - DV); e += NT) {
       const int row = e / (C::DVP - DV), col = DV + e % (C::DVP - DV);
       smem0[C::K_ELEMS + row * C::VROW + col] = 0;
@@ -358,7 +442,9 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   float l_run = 0.0f;        // this lane's part of the running sum (its lane group's keys)
 
   FwdStage<KD, DV, kNCHW, kVecN, kWaves> stage;
-  FwdStageDirect<KD, DV, kWaves> dstage;
+  using DirectStage = typename std::conditional<kNCHW, FwdStageDirect<KD, DV, kWaves>,
+                                                 FwdStagePacked<KD, (kNCHW ? KD : DV), kWaves>>::type;
+  DirectStage dstage;
   if constexpr (kDirect) {
     dstage.init(N, wave, lane);
     dstage.issue(a, bh, kt0, wave, lane, smem0);
@@ -392,7 +478,10 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
         if constexpr (kNCHW)
           kop = lds_read_tr8(ks + (ds * 16 + 8 * g + (i16 >> 2)) * C::KROW + kb * 32 + 16 * t16 +
                                  tr_key_col(i16 & 3), C::KROW);
-        else
+        else if constexpr (kDirect) {
+          const int row = kb * 32 + key_of_row(l32);
+          kop = *reinterpret_cast<const bf16x8*>(ks + row * C::KROW + packed_chunk_pos<KD>(row, ds * 2 + g) * 8);
+        } else
           kop = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + key_of_row(l32)) * C::KROW + ds * 16 + g * 8);
         sacc[kb] = mfma32x32x16(kop, qop[ds], sacc[kb]);
       }
@@ -449,10 +538,16 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         bf16x8 vop;
-        if constexpr (kDirect)
+        if constexpr (kDirect && kNCHW)
           vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW +
                                                  tile_chunk_pos(db * 32 + l32, 2 * s + g) * 8);
-        else if constexpr (kNCHW)
+        else if constexpr (kDirect) {
+          // Two transposed reads, rows r and r + 4, each at its own swizzled chunk.
+          const int r = s * 16 + 8 * g + (i16 >> 2);
+          const int col = db * 32 + 16 * t16 + 4 * (i16 & 3);
+          vop = lds_read_tr8_2(vs + r * C::VROW + packed_chunk_pos<DV>(r, col >> 3) * 8 + (col & 7),
+                               vs + (r + 4) * C::VROW + packed_chunk_pos<DV>(r + 4, col >> 3) * 8 + (col & 7));
+        } else if constexpr (kNCHW)
           vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW + s * 16 + g * 8);
         else
           vop = lds_read_tr8(vs + (s * 16 + 8 * g + (i16 >> 2)) * C::VROW + db * 32 + 16 * t16 + 4 * (i16 & 3),
@@ -712,7 +807,7 @@ struct FwdPlan {
 
 template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
 FwdPlan plan_bf16(int BH, int n_q, int n_k) {
-  using C = FwdCfg<KD, DV, kNCHW, kWaves, kNCHW && kVecN>;
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, direct_staging<KD, kNCHW, kVecN>()>;
   static int occ = -1;   // resident workgroups per CU (the same on every gfx950)
   if (occ < 0) {
     int n = 0;
@@ -734,7 +829,7 @@ FwdPlan plan_bf16(int BH, int n_q, int n_k) {
 // Launches the forward; splits the tail only if `ws` holds the plan's bytes.
 template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
 hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
-  using C = FwdCfg<KD, DV, kNCHW, kWaves, kNCHW && kVecN>;
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, direct_staging<KD, kNCHW, kVecN>()>;
   FwdPlan p = plan_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>(a.BH, a.n_q, a.n_k);
   if (p.tail > 0 && (ws == nullptr || ws_bytes < p.bytes)) {
     p.full += p.tail;
@@ -770,6 +865,12 @@ constexpr int occ_target() {
 // NCHW tiles are staged straight into LDS with buffer loads whose offsets
 // (32-bit) span one batch-head's [4*KD][N] slab: N a multiple of 8 and the
 // slab under 2 GB. Other maps pass through registers.
+// Packed K and V rows are staged straight into LDS with buffer loads whose
+// offsets (32-bit) span one batch-head's [n_k][D] rows: under 2 GB.
+bool packed_direct(int n_k, int D) {
+  return static_cast<int64_t>(n_k) * D * 2 < (int64_t(1) << 31);
+}
+
 bool fused_direct(int KD, int N) {
   return N % 8 == 0 && static_cast<int64_t>(8) * KD * N < (int64_t(1) << 31);
 }
@@ -800,10 +901,10 @@ hipError_t run_f32(FwdArgsF32 a, hipStream_t stream) {
 size_t fa2_fwd_split_bytes(int BH, int n_q, int n_k, int D, bool bf16) {
   if (!bf16) return 0;
   switch (D) {
-    case 16: return split_bytes<16, 16, false>(BH, n_q, n_k, true);
-    case 32: return split_bytes<32, 32, false>(BH, n_q, n_k, true);
-    case 64: return split_bytes<64, 64, false>(BH, n_q, n_k, true);
-    case 128: return split_bytes<128, 128, false>(BH, n_q, n_k, true);
+    case 16: return split_bytes<16, 16, false>(BH, n_q, n_k, packed_direct(n_k, 16));
+    case 32: return split_bytes<32, 32, false>(BH, n_q, n_k, packed_direct(n_k, 32));
+    case 64: return split_bytes<64, 64, false>(BH, n_q, n_k, packed_direct(n_k, 64));
+    case 128: return split_bytes<128, 128, false>(BH, n_q, n_k, packed_direct(n_k, 128));
   }
   return 0;
 }
@@ -846,10 +947,10 @@ hipError_t launch_fa2_fwd(const void* q, const void* k, const void* v, void* o, 
   a.n_k = n_k;
   a.c = scale * kLog2e;
   switch (D) {
-    case 16: return run_bf16<16, 16, false>(a, true, ws, ws_bytes, stream);
-    case 32: return run_bf16<32, 32, false>(a, true, ws, ws_bytes, stream);
-    case 64: return run_bf16<64, 64, false>(a, true, ws, ws_bytes, stream);
-    case 128: return run_bf16<128, 128, false>(a, true, ws, ws_bytes, stream);
+    case 16: return run_bf16<16, 16, false>(a, packed_direct(n_k, 16), ws, ws_bytes, stream);
+    case 32: return run_bf16<32, 32, false>(a, packed_direct(n_k, 32), ws, ws_bytes, stream);
+    case 64: return run_bf16<64, 64, false>(a, packed_direct(n_k, 64), ws, ws_bytes, stream);
+    case 128: return run_bf16<128, 128, false>(a, packed_direct(n_k, 128), ws, ws_bytes, stream);
   }
   return hipErrorInvalidValue;
 }

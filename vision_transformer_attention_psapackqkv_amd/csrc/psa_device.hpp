@@ -69,6 +69,15 @@ __device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* p, int row) {
   return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
 }
 
+// The same operand with the two reads' addresses given separately (tiles
+// whose rows are swizzled differently).
+__device__ __forceinline__ bf16x8 lds_read_tr8_2(const uint16_t* p_lo, const uint16_t* p_hi) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p_lo));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p_hi));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+}
+
 // Index held by row rho (0..31) of a 32-row accumulator block whose A operand
 // was read with tr_key_col: 8h + 4g + e -> 8g + 4h + e inside each 16-row half.
 // Accumulator element r of lane group g then holds index 16*(r/8) + 8g + r%8:
