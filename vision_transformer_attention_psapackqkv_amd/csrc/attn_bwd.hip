@@ -141,10 +141,11 @@ struct DkdvTile {
   }
 };
 
-// Head dims up to 32: registers capped for three workgroups per CU (measured
-// faster than two with more registers).
+// Registers capped for three workgroups per CU up to head dim 32 and for two
+// at 64 (both fit without spilling; measured faster than fewer workgroups with
+// more registers); head dim 128 needs a whole SIMD's register file.
 template <int D, int kWaves>
-__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dkdv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bwd_dkdv_bf16(BwdArgs a) {
   using Tile = DkdvTile<D, kWaves>;
   constexpr int BQ = Tile::BQ;
   constexpr int NDS = D / 16;
@@ -310,7 +311,7 @@ struct DqTile {
 };
 
 template <int D, int kWaves>
-__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : 1) void bwd_dq_bf16(BwdArgs a) {
+__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bwd_dq_bf16(BwdArgs a) {
   using Tile = DqTile<D, kWaves>;
   constexpr int BN = Tile::BN;
   constexpr int NDS = D / 16;
