@@ -856,10 +856,12 @@ hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream)
 
 // Workgroups per CU the registers must allow for head dims up to 64: three
 // where the LDS also holds three (directly staged NCHW tiles, key_dim 64),
-// else two. Head dim 128 runs one.
+// else two. Head dim 128: two for fa2_fwd (220 VGPRs, no spills; with no cap
+// the compiler took 296 and ran one), one for the fused kernel (value width
+// 256 needs more than half the register file).
 template <int KD, bool kNCHW, bool kVecN>
 constexpr int occ_target() {
-  return KD > 64 ? 1 : (kNCHW && kVecN && KD == 64) ? 3 : 2;
+  return KD > 64 ? (kNCHW ? 1 : 2) : (kNCHW && kVecN && KD == 64) ? 3 : 2;
 }
 
 // NCHW tiles are staged straight into LDS with buffer loads whose offsets
