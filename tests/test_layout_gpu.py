@@ -11,7 +11,8 @@ from tests.gpu_helpers import announce, bits, device
 pytestmark = pytest.mark.gpu
 
 # (B, heads, key_dim, H, W, dtype): the workload maps, then ragged pixel counts
-# (N = 1, 7, 63, 65, 400 and N not a multiple of 8 or 4) at every key_dim.
+# (N = 1, 7, 63, 65, 400 and N not a multiple of 8 or 4) at every key_dim, then
+# ragged staged tiles.
 SHAPES = [
     (1, 1, 16, 8, 8, "f32"),
     (8, 4, 32, 20, 20, "bf16"),
@@ -24,6 +25,13 @@ SHAPES = [
     (2, 1, 64, 2, 2, "f32"),
     (1, 1, 128, 9, 7, "f32"),
     (2, 2, 64, 16, 16, "bf16"),
+    # N a multiple of 8 (4 for f32) but not of the staged tile's pixel count
+    # (16 KB / (key_dim * element size)): several tiles and a short last one.
+    (2, 1, 128, 8, 10, "bf16"),
+    (1, 2, 128, 12, 12, "f32"),
+    (2, 2, 16, 24, 24, "bf16"),
+    (1, 1, 32, 12, 12, "f32"),
+    (1, 2, 64, 9, 24, "bf16"),
 ]
 
 

@@ -8,46 +8,25 @@
 // [N, KD] matrix. So every op is a batch of [KD, N] <-> [N, KD] transposes
 // with a slab-index permutation, and each is bound by HBM bandwidth.
 //
-// Each thread moves one VEC x VEC block (VEC = 16 bytes / element size):
-// VEC 16-byte loads, a transpose in registers, VEC 16-byte stores. Threads are
-// laid out with the d-block index fastest, so every load instruction of a
-// wave covers whole 128-byte runs of NCHW rows and every store instruction
-// whole packed rows. No LDS is needed. Rows whose start is not 16-byte
-// aligned (N not a multiple of VEC) take a scalar kernel instead. Measured on
-// MI355X at the 80x80 map, 256-thread workgroups suit pack and 128-thread
-// workgroups suit merge and extract (both above a plain device copy).
+// A workgroup moves one tile of a slab (all KD channels x 16 KB / (KD * elt)
+// pixels) through LDS: 16-byte loads along the side the data is contiguous on,
+// the transpose between LDS and registers, 16-byte stores along the other
+// side, so that every wave instruction reads or writes 1 KB of contiguous runs
+// on both sides (whole channel-row runs on the NCHW side, whole consecutive
+// rows on the packed side). Rows whose start is not 16-byte aligned (N not a
+// multiple of 16 bytes / element size) take a scalar kernel instead. Measured
+// on MI355X at the 80x80 map, this beats an 8x8-block register transpose (whose
+// wave instructions touch 8 separate 128-byte runs) by ~4 % and a plain device
+// copy of the same bytes by ~15 %.
+#include <type_traits>
+
 #include "psa_device.hpp"
 #include "psa_launch.hpp"
 
 namespace psa {
 namespace {
 
-constexpr int kThreads = 256;            // scalar kernel
-constexpr int kThreadsToRows = 256;      // pack
-constexpr int kThreadsToNchw = 128;      // merge, extract
-
-// 8x8 transpose of 16-bit elements: in[r] holds row r (8 elements, two per
-// 32-bit word, element 2w in the low half of word w); out[c] receives column c.
-__device__ __forceinline__ void transpose_block(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = in[2 * w][c >> 1];
-      const uint32_t hi = in[2 * w + 1][c >> 1];
-      out[c][w] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-  }
-}
-
-// 4x4 transpose of 32-bit elements.
-__device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&out)[4]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) out[c][w] = in[w][c];
-  }
-}
+constexpr int kThreads = 256;   // scalar kernel
 
 struct SlabGeom {
   int BH, KD, N;
@@ -65,44 +44,114 @@ __device__ __forceinline__ void slab_offsets(const SlabGeom& g, int t, int64_t& 
   rows_off = (static_cast<int64_t>(g.slot0 + s) * g.BH + bh) * slab;
 }
 
+// One tile = all KD channels x PX pixels of one slab (16 KB of data), staged in
+// LDS so that both global sides move in long contiguous runs: 16-byte chunk q
+// of the NCHW side is (row q / CPR, column q % CPR), so one wave instruction
+// covers 1 KB of whole channel-row runs; chunk q of the packed side is (pixel
+// q / (KD / VEC), channel block q % (KD / VEC)), so one wave instruction covers
+// whole consecutive packed rows (1 KB contiguous at KD = 64). The transpose
+// happens between LDS and registers, one element at a time on the side the
+// chunk does not run along. LDS chunk columns are XOR-swizzled by the row's
+// channel block, so the 8 rows (4 for f32) one packed-side chunk gathers from
+// sit in different bank groups.
+constexpr int kThreadsLds = 256;
+constexpr int kTileBytes = 16384;
+
+template <int kElt>
+struct Word;
+template <>
+struct Word<2> { using T = uint16_t; };
+template <>
+struct Word<4> { using T = uint32_t; };
+
 // kToRows = true: NCHW [KD, N] slabs -> packed [N, KD] slabs (pack).
 // kToRows = false: packed [N, KD] slabs -> NCHW [KD, N] slabs (merge, extract).
-template <int kEltBytes, bool kToRows, int kTh = kToRows ? kThreadsToRows : kThreadsToNchw>
-__global__ __launch_bounds__(kTh) void transpose_slabs_vec(const void* __restrict__ src_v,
-                                                           void* __restrict__ dst_v,
-                                                           SlabGeom g, int tiles_per_slab) {
-  constexpr int VEC = 16 / kEltBytes;
-  const int DB = g.KD / VEC;             // d-blocks per row of the packed side
-  const int NBW = kTh / DB;              // n-blocks per workgroup
+template <int kElt, int KD, bool kToRows>
+__global__ __launch_bounds__(kThreadsLds) void transpose_slabs_lds(const void* __restrict__ src_v,
+                                                                   void* __restrict__ dst_v,
+                                                                   SlabGeom g, int tiles_per_slab) {
+  using T = typename Word<kElt>::T;
+  constexpr int VEC = 16 / kElt;                 // elements per 16-byte chunk
+  constexpr int PX = kTileBytes / (KD * kElt);   // pixels per tile
+  constexpr int CPR = PX / VEC;                  // chunks per channel row of a tile (>= 8)
+  constexpr int DBN = KD / VEC;                  // chunks per packed row
+  constexpr int PER = KD * CPR / kThreadsLds;    // chunks per thread (4)
+  static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0 && KD * CPR == PER * kThreadsLds, "tile shape");
+  __shared__ __attribute__((aligned(16))) T lds[KD * PX];
+
   const int t = blockIdx.x / tiles_per_slab;
   const int tile = blockIdx.x - t * tiles_per_slab;
-  const int db = threadIdx.x % DB;
-  const int nb = tile * NBW + threadIdx.x / DB;
-  if (nb * VEC >= g.N) return;
-
+  const int p0 = tile * PX;
+  const int np = min(PX, g.N - p0);   // pixels of this tile; a multiple of VEC
   int64_t nchw_off, rows_off;
   slab_offsets(g, t, nchw_off, rows_off);
-  // Element offsets of this thread's block on each side.
-  const int64_t nchw_base = nchw_off + static_cast<int64_t>(db) * VEC * g.N + nb * VEC;
-  const int64_t rows_base = rows_off + static_cast<int64_t>(nb) * VEC * g.KD + db * VEC;
-  const char* src = static_cast<const char*>(src_v);
-  char* dst = static_cast<char*>(dst_v);
-  // Row r of the block on the source side, column c on the destination side.
-  const int64_t src_base = kToRows ? nchw_base : rows_base;
-  const int64_t src_stride = kToRows ? g.N : g.KD;
-  const int64_t dst_base = kToRows ? rows_base : nchw_base;
-  const int64_t dst_stride = kToRows ? g.KD : g.N;
+  const T* src = static_cast<const T*>(src_v);
+  T* dst = static_cast<T*>(dst_v);
+  // LDS element index of (channel row, pixel) inside the tile.
+  auto at = [](int row, int px) { return row * PX + (((px / VEC) ^ ((row / VEC) & 7)) * VEC) + px % VEC; };
 
-  u32x4 in[VEC], out[VEC];
+  // Only the global stores are guarded. Loads past the tile's last pixel (the
+  // short last tile of a slab) are clamped to its last chunk, so every load is
+  // unconditional and all of a thread's loads are in flight together (a load
+  // under a branch would be waited for inside that branch); LDS positions past
+  // it hold those duplicates and are never stored.
+  u32x4 v[PER];
+  if constexpr (kToRows) {
 #pragma unroll
-  for (int r = 0; r < VEC; ++r) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(src + (src_base + r * src_stride) * kEltBytes);
-    in[r] = kToRows ? ldg_nt(p) : *p;   // non-temporal reads: measured faster for pack only
+    for (int u = 0; u < PER; ++u) {
+      const int q = u * kThreadsLds + threadIdx.x, row = q / CPR, col = q % CPR;
+      const int p = min(col * VEC, np - VEC);
+      v[u] = ldg_nt(reinterpret_cast<const u32x4*>(src + nchw_off + static_cast<int64_t>(row) * g.N + p0 + p));
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = u * kThreadsLds + threadIdx.x, row = q / CPR, col = q % CPR;
+      *reinterpret_cast<u32x4*>(&lds[at(row, col * VEC)]) = v[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = u * kThreadsLds + threadIdx.x, px = q / DBN, cb = q % DBN;
+      u32x4 w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (kElt == 2)
+          w[k] = uint32_t(lds[at(cb * VEC + 2 * k, px)]) | (uint32_t(lds[at(cb * VEC + 2 * k + 1, px)]) << 16);
+        else
+          w[k] = lds[at(cb * VEC + k, px)];
+      }
+      if (px < np)
+        stg_nt(reinterpret_cast<u32x4*>(dst + rows_off + static_cast<int64_t>(p0 + px) * KD + cb * VEC), w);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = u * kThreadsLds + threadIdx.x, px = q / DBN, cb = q % DBN;
+      const int p = min(px, np - 1);
+      v[u] = ldg_nt(reinterpret_cast<const u32x4*>(src + rows_off + static_cast<int64_t>(p0 + p) * KD + cb * VEC));
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = u * kThreadsLds + threadIdx.x, px = q / DBN, cb = q % DBN;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (kElt == 2) {
+          lds[at(cb * VEC + 2 * k, px)] = static_cast<T>(v[u][k] & 0xFFFFu);
+          lds[at(cb * VEC + 2 * k + 1, px)] = static_cast<T>(v[u][k] >> 16);
+        } else {
+          lds[at(cb * VEC + k, px)] = v[u][k];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = u * kThreadsLds + threadIdx.x, row = q / CPR, col = q % CPR;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&lds[at(row, col * VEC)]);
+      if (col * VEC < np)
+        stg_nt(reinterpret_cast<u32x4*>(dst + nchw_off + static_cast<int64_t>(row) * g.N + p0 + col * VEC), w);
+    }
   }
-  transpose_block(in, out);
-#pragma unroll
-  for (int c = 0; c < VEC; ++c)
-    stg_nt(reinterpret_cast<u32x4*>(dst + (dst_base + c * dst_stride) * kEltBytes), out[c]);
 }
 
 // Any N: one thread per element, consecutive threads walk the packed side.
@@ -126,20 +175,34 @@ __global__ __launch_bounds__(kThreads) void transpose_slabs_scalar(const T* __re
     dst[nchw_i] = src[rows_i];
 }
 
+template <int kElt, bool kToRows>
+void launch_lds(const void* src, void* dst, SlabGeom g, int n_slabs, hipStream_t stream) {
+  auto go = [&](auto kd) {
+    constexpr int KD = decltype(kd)::value;
+    constexpr int PX = kTileBytes / (KD * kElt);
+    const int tiles = (g.N + PX - 1) / PX;
+    const dim3 grid(static_cast<unsigned>(n_slabs) * tiles);
+    transpose_slabs_lds<kElt, KD, kToRows><<<grid, kThreadsLds, 0, stream>>>(src, dst, g, tiles);
+  };
+  switch (g.KD) {
+    case 16: go(std::integral_constant<int, 16>{}); break;
+    case 32: go(std::integral_constant<int, 32>{}); break;
+    case 64: go(std::integral_constant<int, 64>{}); break;
+    default: go(std::integral_constant<int, 128>{}); break;
+  }
+}
+
 template <bool kToRows>
 hipError_t launch_transpose(const void* src, void* dst, SlabGeom g, int elt_bytes,
                             hipStream_t stream) {
   const int n_slabs = g.BH * g.slots;
   const int vec = 16 / elt_bytes;
+  if (g.KD != 16 && g.KD != 32 && g.KD != 64 && g.KD != 128) return hipErrorInvalidValue;
   if (g.N % vec == 0) {
-    constexpr int th = kToRows ? kThreadsToRows : kThreadsToNchw;
-    const int nbw = th / (g.KD / vec);
-    const int tiles = (g.N / vec + nbw - 1) / nbw;
-    const dim3 grid(static_cast<unsigned>(n_slabs) * tiles);
     if (elt_bytes == 2)
-      transpose_slabs_vec<2, kToRows><<<grid, th, 0, stream>>>(src, dst, g, tiles);
+      launch_lds<2, kToRows>(src, dst, g, n_slabs, stream);
     else
-      transpose_slabs_vec<4, kToRows><<<grid, th, 0, stream>>>(src, dst, g, tiles);
+      launch_lds<4, kToRows>(src, dst, g, n_slabs, stream);
   } else {
     const int64_t per_slab = static_cast<int64_t>(g.N) * g.KD;
     const int tiles = static_cast<int>((per_slab + kThreads - 1) / kThreads);
