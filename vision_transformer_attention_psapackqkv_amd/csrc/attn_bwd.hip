@@ -97,29 +97,29 @@ struct DkdvTile {
   static constexpr int CHUNKS = BQ * D / 8;        // 16-byte pieces of the Q (and of the dO) rows
   static constexpr int PER = (CHUNKS + NT - 1) / NT;
 
+  // Raw loads of the next tile. Every load is unconditional (chunk and row
+  // indices clamped into range) and nothing reads the loaded registers until
+  // store() at the end of the current tile, so the loads stay in flight while
+  // it is computed; store() zeroes the rows past n_q.
   u32x4 qr[PER], gr[PER];
   float l2, dl;
+  int rows;   // rows of this tile that exist (n_q - first row)
 
   __device__ __forceinline__ void load(const BwdArgs& a, int bh, int qt, int tid) {
     const int q0 = qt * BQ;
+    rows = a.n_q - q0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
-      if (c < CHUNKS) {
-        const int r = c / (D / 8), cb = c % (D / 8);
-        const int qq = q0 + r;
-        const int64_t off = (static_cast<int64_t>(bh) * a.n_q + qq) * D + cb * 8;
-        qr[i] = (qq < a.n_q) ? load16(a.q + off) : zero4();
-        gr[i] = (qq < a.n_q) ? load16(a.dout + off) : zero4();
-      }
+      const int cc = c < CHUNKS ? c : CHUNKS - 1;
+      const int r = cc / (D / 8), cb = cc % (D / 8);
+      const int64_t off = (static_cast<int64_t>(bh) * a.n_q + min(q0 + r, a.n_q - 1)) * D + cb * 8;
+      qr[i] = load16(a.q + off);
+      gr[i] = load16(a.dout + off);
     }
-    if (tid < BQ) {
-      const int qq = q0 + tid;
-      const bool ok = qq < a.n_q;
-      // Rows past n_q get P = 0 (LSE = +inf) and Delta = 0.
-      l2 = ok ? a.lse[static_cast<int64_t>(bh) * a.n_q + qq] * kLog2e : INFINITY;
-      dl = ok ? a.delta[static_cast<int64_t>(bh) * a.n_q + qq] : 0.0f;
-    }
+    const int64_t i = static_cast<int64_t>(bh) * a.n_q + min(q0 + (tid < BQ ? tid : BQ - 1), a.n_q - 1);
+    l2 = a.lse[i];
+    dl = a.delta[i];
   }
 
   __device__ __forceinline__ void store(char* buf, int tid) const {
@@ -130,13 +130,16 @@ struct DkdvTile {
       const int c = tid + i * NT;
       if (c < CHUNKS) {
         const int r = c / (D / 8), cb = c % (D / 8);
-        *reinterpret_cast<u32x4*>(h + OFF_Q + r * RSTR + cb * 8) = qr[i];
-        *reinterpret_cast<u32x4*>(h + OFF_DO + r * RSTR + cb * 8) = gr[i];
+        const bool ok = r < rows;
+        *reinterpret_cast<u32x4*>(h + OFF_Q + r * RSTR + cb * 8) = ok ? qr[i] : zero4();
+        *reinterpret_cast<u32x4*>(h + OFF_DO + r * RSTR + cb * 8) = ok ? gr[i] : zero4();
       }
     }
     if (tid < BQ) {
-      f[tid] = l2;
-      f[BQ + tid] = dl;
+      // Rows past n_q get P = 0 (LSE = +inf) and Delta = 0.
+      const bool ok = tid < rows;
+      f[tid] = ok ? l2 * kLog2e : INFINITY;
+      f[BQ + tid] = ok ? dl : 0.0f;
     }
   }
 };
@@ -160,12 +163,22 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
   const bool k_ok = key < a.n_k;
 
   // This lane's key and value rows as B operands: K[key][16ds + 8g + j].
+  // Keys past n_k load row n_k - 1 (all loads unconditional, in flight
+  // together) and are zeroed afterwards.
   bf16x8 kop[NDS], vop[NDS];
+  {
+    u32x4 kr[NDS], vr[NDS];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    const int64_t off = (static_cast<int64_t>(bh) * a.n_k + key) * D + ds * 16 + g * 8;
-    kop[ds] = as_bf16x8(k_ok ? load16(a.k + off) : zero4());
-    vop[ds] = as_bf16x8(k_ok ? load16(a.v + off) : zero4());
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int64_t off = (static_cast<int64_t>(bh) * a.n_k + min(key, a.n_k - 1)) * D + ds * 16 + g * 8;
+      kr[ds] = load16(a.k + off);
+      vr[ds] = load16(a.v + off);
+    }
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      kop[ds] = as_bf16x8(k_ok ? kr[ds] : zero4());
+      vop[ds] = as_bf16x8(k_ok ? vr[ds] : zero4());
+    }
   }
   f32x16 dk_acc[NDB], dv_acc[NDB];
 #pragma unroll
@@ -279,21 +292,24 @@ struct DqTile {
   static constexpr int CHUNKS = BN * D / 8;        // 16-byte pieces of the K (and of the V) rows
   static constexpr int PER = (CHUNKS + NT - 1) / NT;
 
+  // Raw loads of the next tile: unconditional (indices clamped into range),
+  // not read until store() at the end of the current tile, which zeroes the
+  // rows past n_k.
   u32x4 kr[PER];
   u32x4 vr[PER];
+  int rows;   // rows of this tile that exist (n_k - first row)
 
   __device__ __forceinline__ void load(const BwdArgs& a, int bh, int kt, int tid) {
     const int m0 = kt * BN;
+    rows = a.n_k - m0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
-      if (c < CHUNKS) {
-        const int r = c / (D / 8), cb = c % (D / 8);
-        const int m = m0 + r;
-        const int64_t off = (static_cast<int64_t>(bh) * a.n_k + m) * D + cb * 8;
-        kr[i] = (m < a.n_k) ? load16(a.k + off) : zero4();
-        vr[i] = (m < a.n_k) ? load16(a.v + off) : zero4();
-      }
+      const int cc = c < CHUNKS ? c : CHUNKS - 1;
+      const int r = cc / (D / 8), cb = cc % (D / 8);
+      const int64_t off = (static_cast<int64_t>(bh) * a.n_k + min(m0 + r, a.n_k - 1)) * D + cb * 8;
+      kr[i] = load16(a.k + off);
+      vr[i] = load16(a.v + off);
     }
   }
 
@@ -303,8 +319,9 @@ struct DqTile {
       const int c = tid + i * NT;
       if (c < CHUNKS) {
         const int r = c / (D / 8), cb = c % (D / 8);
-        *reinterpret_cast<u32x4*>(buf + OFF_K + r * RSTR + cb * 8) = kr[i];
-        *reinterpret_cast<u32x4*>(buf + OFF_V + r * RSTR + cb * 8) = vr[i];
+        const bool ok = r < rows;
+        *reinterpret_cast<u32x4*>(buf + OFF_K + r * RSTR + cb * 8) = ok ? kr[i] : zero4();
+        *reinterpret_cast<u32x4*>(buf + OFF_V + r * RSTR + cb * 8) = ok ? vr[i] : zero4();
       }
     }
   }
@@ -326,15 +343,29 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
   const int q = qt * BM + wave * 32 + l32;
   const bool q_ok = q < a.n_q;
 
+  // Queries past n_q load row n_q - 1 (all loads unconditional, in flight
+  // together) and are zeroed afterwards.
   bf16x8 qop[NDS], gop[NDS];
+  float l2, dl;
+  {
+    const int qc = min(q, a.n_q - 1);
+    u32x4 qr[NDS], gr[NDS];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    const int64_t off = (static_cast<int64_t>(bh) * a.n_q + q) * D + ds * 16 + g * 8;
-    qop[ds] = as_bf16x8(q_ok ? load16(a.q + off) : zero4());
-    gop[ds] = as_bf16x8(q_ok ? load16(a.dout + off) : zero4());
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int64_t off = (static_cast<int64_t>(bh) * a.n_q + qc) * D + ds * 16 + g * 8;
+      qr[ds] = load16(a.q + off);
+      gr[ds] = load16(a.dout + off);
+    }
+    const float lv = a.lse[static_cast<int64_t>(bh) * a.n_q + qc];
+    const float dv = a.delta[static_cast<int64_t>(bh) * a.n_q + qc];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      qop[ds] = as_bf16x8(q_ok ? qr[ds] : zero4());
+      gop[ds] = as_bf16x8(q_ok ? gr[ds] : zero4());
+    }
+    l2 = q_ok ? lv * kLog2e : 0.0f;
+    dl = q_ok ? dv : 0.0f;
   }
-  const float l2 = q_ok ? a.lse[static_cast<int64_t>(bh) * a.n_q + q] * kLog2e : 0.0f;
-  const float dl = q_ok ? a.delta[static_cast<int64_t>(bh) * a.n_q + q] : 0.0f;
   f32x16 dq_acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

@@ -396,20 +396,49 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     }
   }
 
+  // The first key tile's direct loads go out first, so that their round trip
+  // overlaps the V residual copy and the Q loads below.
+  FwdStage<KD, DV, kNCHW, kVecN, kWaves> stage;
+  using DirectStage = typename std::conditional<kNCHW, FwdStageDirect<KD, DV, kWaves>,
+                                                 FwdStagePacked<KD, (kNCHW ? KD : DV), kWaves>>::type;
+  DirectStage dstage;
+  if constexpr (kDirect) {
+    dstage.init(N, wave, lane);
+    dstage.issue(a, bh, kt0, wave, lane, smem0);
+  }
+
   // V residual: copy this tile's pixel columns of the V channels (NCHW only;
-  // the first piece of a split tile does it).
+  // the first piece of a split tile does it). With 16-byte rows the loads of a
+  // batch are unconditional (chunks past the map's last pixel re-read its last
+  // chunk; only the stores are guarded), so they are all in flight together.
   if constexpr (kNCHW) {
     if (a.vres != nullptr && piece == 0) {
       const int n0 = qt * BM;
       constexpr int CPR = BM / 8;   // 8-pixel chunks per channel row
-      for (int c = tid; c < DV * CPR; c += NT) {
-        const int dv = c / CPR, cb = c % CPR;
-        const int n = n0 + cb * 8;
-        const uint16_t* src = a.v + (static_cast<int64_t>(bh) * 4 * KD + 2 * KD + dv) * N + n;
-        uint16_t* dst = a.vres + (static_cast<int64_t>(bh) * DV + dv) * N + n;
-        if constexpr (kVecN) {
-          if (n < N) stg_nt(reinterpret_cast<u32x4*>(dst), load16(src));
-        } else {
+      constexpr int TOTAL = DV * CPR;
+      if constexpr (kVecN) {
+        static_assert(TOTAL % NT == 0, "V residual chunks per thread");
+        constexpr int PER = TOTAL / NT;
+        constexpr int BATCH = PER < 8 ? PER : 8;
+#pragma unroll
+        for (int u0 = 0; u0 < PER; u0 += BATCH) {
+          u32x4 r[BATCH];
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int c = (u0 + u) * NT + tid, dv = c / CPR, n = n0 + (c % CPR) * 8;
+            r[u] = load16(a.v + (static_cast<int64_t>(bh) * 4 * KD + 2 * KD + dv) * N + min(n, N - 8));
+          }
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int c = (u0 + u) * NT + tid, dv = c / CPR, n = n0 + (c % CPR) * 8;
+            if (n < N) stg_nt(reinterpret_cast<u32x4*>(a.vres + (static_cast<int64_t>(bh) * DV + dv) * N + n), r[u]);
+          }
+        }
+      } else {
+        for (int c = tid; c < TOTAL; c += NT) {
+          const int dv = c / CPR, n = n0 + (c % CPR) * 8;
+          const uint16_t* src = a.v + (static_cast<int64_t>(bh) * 4 * KD + 2 * KD + dv) * N + n;
+          uint16_t* dst = a.vres + (static_cast<int64_t>(bh) * DV + dv) * N + n;
           for (int e = 0; e < 8; ++e)
             if (n + e < N) dst[e] = src[e];
         }
@@ -417,20 +446,22 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     }
   }
 
-  // This lane's Q operands: Q[q_row][16*ds + 8*g + j], j = 0..7.
+  // This lane's Q operands: Q[q_row][16*ds + 8*g + j], j = 0..7. Rows past
+  // n_q load row n_q - 1 (every load unconditional, all in flight together)
+  // and are zeroed afterwards.
   bf16x8 qop[NDS];
+  {
+    const int qr = min(q_row, a.n_q - 1);
+    u32x4 raw[NDS];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    u32x4 raw = zero4();
-    if (q_ok) {
-      if constexpr (kNCHW) {
-        const uint16_t* src = a.q + (static_cast<int64_t>(bh) * 4 * KD + ds * 16 + g * 8) * N + q_row;
-        raw = gather8(src, N, 0, 8);
-      } else {
-        raw = load16(a.q + (static_cast<int64_t>(bh) * a.n_q + q_row) * KD + ds * 16 + g * 8);
-      }
+    for (int ds = 0; ds < NDS; ++ds) {
+      if constexpr (kNCHW)
+        raw[ds] = gather8(a.q + (static_cast<int64_t>(bh) * 4 * KD + ds * 16 + g * 8) * N + qr, N, 0, 8);
+      else
+        raw[ds] = load16(a.q + (static_cast<int64_t>(bh) * a.n_q + qr) * KD + ds * 16 + g * 8);
     }
-    qop[ds] = as_bf16x8(raw);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qop[ds] = as_bf16x8(q_ok ? raw[ds] : zero4());
   }
 
   f32x16 oacc[NDB];
@@ -439,16 +470,12 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
   float m_run = -INFINITY;   // running max of scale*log2(e)*S
+  float m_thr = -INFINITY;   // (m_run + 8) / (scale*log2(e)): the rescale threshold on raw scores
+  const float inv_c = 1.0f / a.c;
   float l_run = 0.0f;        // this lane's part of the running sum (its lane group's keys)
 
-  FwdStage<KD, DV, kNCHW, kVecN, kWaves> stage;
-  using DirectStage = typename std::conditional<kNCHW, FwdStageDirect<KD, DV, kWaves>,
-                                                 FwdStagePacked<KD, (kNCHW ? KD : DV), kWaves>>::type;
-  DirectStage dstage;
   if constexpr (kDirect) {
-    dstage.init(N, wave, lane);
-    dstage.issue(a, bh, kt0, wave, lane, smem0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of tile kt0 landed
   } else {
     stage.load(a, bh, kt0, tid);
     stage.store(smem0, tid);
@@ -505,13 +532,14 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = fmaxf(mx, lane_xor32(mx, g));
-    const float m_tile = mx * a.c;
     // The running max only moves when some lane's tile max exceeds it by more
-    // than 8 (log2 units): until then P <= 2^8, harmless in fp32 and bf16.
-    if (__any(m_tile > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, m_tile);
+    // than 8 (log2 units): until then P <= 2^8, harmless in fp32 and bf16. The
+    // test is on the raw scores, against the threshold kept since the last move.
+    if (__any(mx > m_thr)) {
+      const float m_new = fmaxf(m_run, mx * a.c);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
+      m_thr = (m_run + 8.0f) * inv_c;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)

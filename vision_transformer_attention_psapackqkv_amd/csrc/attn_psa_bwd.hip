@@ -201,15 +201,23 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
   }
 
   // B operands of S and dP: K[key][16ds + 8g + j] and V[key][16vs + 8g + j].
+  // Keys past N load pixel N - 1 (every load unconditional, all in flight
+  // together) and are zeroed afterwards.
   bf16x8 kop[NDS], vop[NVS];
+  {
+    const int kc = min(key, N - 1);
+    u32x4 kr[NDS], vr[NVS];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds)
-    kop[ds] = as_bf16x8(k_ok ? gather8(qkv + static_cast<int64_t>(KD + ds * 16 + g * 8) * N + key, N, 0, 8)
-                             : zero4());
+    for (int ds = 0; ds < NDS; ++ds)
+      kr[ds] = gather8(qkv + static_cast<int64_t>(KD + ds * 16 + g * 8) * N + kc, N, 0, 8);
 #pragma unroll
-  for (int vs = 0; vs < NVS; ++vs)
-    vop[vs] = as_bf16x8(k_ok ? gather8(qkv + static_cast<int64_t>(2 * KD + vs * 16 + g * 8) * N + key, N, 0, 8)
-                             : zero4());
+    for (int vs = 0; vs < NVS; ++vs)
+      vr[vs] = gather8(qkv + static_cast<int64_t>(2 * KD + vs * 16 + g * 8) * N + kc, N, 0, 8);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) kop[ds] = as_bf16x8(k_ok ? kr[ds] : zero4());
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs) vop[vs] = as_bf16x8(k_ok ? vr[vs] : zero4());
+  }
   f32x16 dk[NDK], dv[NDV];
 #pragma unroll
   for (int b = 0; b < NDK; ++b)
@@ -374,16 +382,29 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
     }
   }
 
-  // B operands: Q[q][16ds + 8g + j] and dO[q][16vs + 8g + j].
+  // B operands: Q[q][16ds + 8g + j] and dO[q][16vs + 8g + j]. Queries past N
+  // load pixel N - 1 (every load unconditional, all in flight together) and
+  // are zeroed afterwards.
   bf16x8 qop[NDS], gop[NVS];
+  float l2, dl;
+  {
+    const int qc = min(q, N - 1);
+    u32x4 qr[NDS], gr[NVS];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds)
-    qop[ds] = as_bf16x8(q_ok ? gather8(qkv + static_cast<int64_t>(ds * 16 + g * 8) * N + q, N, 0, 8) : zero4());
+    for (int ds = 0; ds < NDS; ++ds)
+      qr[ds] = gather8(qkv + static_cast<int64_t>(ds * 16 + g * 8) * N + qc, N, 0, 8);
 #pragma unroll
-  for (int vs = 0; vs < NVS; ++vs)
-    gop[vs] = as_bf16x8(q_ok ? gather8(dout + static_cast<int64_t>(vs * 16 + g * 8) * N + q, N, 0, 8) : zero4());
-  const float l2 = q_ok ? a.lse2[static_cast<int64_t>(bh) * N + q] : INFINITY;
-  const float dl = q_ok ? a.delta[static_cast<int64_t>(bh) * N + q] : 0.0f;
+    for (int vs = 0; vs < NVS; ++vs)
+      gr[vs] = gather8(dout + static_cast<int64_t>(vs * 16 + g * 8) * N + qc, N, 0, 8);
+    const float lv = a.lse2[static_cast<int64_t>(bh) * N + qc];
+    const float dv = a.delta[static_cast<int64_t>(bh) * N + qc];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qop[ds] = as_bf16x8(q_ok ? qr[ds] : zero4());
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs) gop[vs] = as_bf16x8(q_ok ? gr[vs] : zero4());
+    l2 = q_ok ? lv : INFINITY;
+    dl = q_ok ? dv : 0.0f;
+  }
   f32x16 dq[NDB];
 #pragma unroll
   for (int b = 0; b < NDB; ++b)
