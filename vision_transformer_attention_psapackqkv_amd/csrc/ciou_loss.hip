@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kThreads) void ciou_fwd_vec(const float* __restrict
     p[c] = ldg_nt(P + c * N4 + i);
     g[c] = ldg_nt(G + c * N4 + i);
   }
+  __builtin_amdgcn_sched_barrier(0);   // all eight loads ahead of the arithmetic
   f4 lo, io, vo, ao;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -197,6 +198,9 @@ __global__ __launch_bounds__(kThreads) void ciou_bwd_vec(
   const f4 vv = ldg_nt(reinterpret_cast<const f4*>(v) + i);
   const f4 a = ldg_nt(reinterpret_cast<const f4*>(alpha) + i);
   const f4 dl = ldg_nt(reinterpret_cast<const f4*>(dloss) + i);
+  // Keep all twelve loads ahead of the arithmetic (the scheduler would otherwise
+  // sink some of them to their first use, each then waited for on its own).
+  __builtin_amdgcn_sched_barrier(0);
   f4 o[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
