@@ -119,3 +119,29 @@ def test_psa_attention_bwd_repeatable():
     a = _run(qkv, dout, dv, h, KD, dev)
     b = _run(qkv, dout, dv, h, KD, dev)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("with_v_grad", [True, False])
+def test_autograd_wrapper(with_v_grad):
+    """psa_attention (torch autograd over psa_attention_fwd / psa_attention_bwd): its outputs
+    equal the forward entry point's bit for bit, qkv.grad equals the backward entry point's
+    bit for bit (the V-residual gradient absent when the loss does not use it), and both
+    match the oracle."""
+    dev = device()
+    B, h, KD, H, W = 2, 2, 32, 12, 12
+    announce(f"autograd wrapper v_grad={with_v_grad}")
+    qkv, dout, dv = _inputs(B, h, KD, H, W, seed=4242, with_dv=with_v_grad)
+    x = qkv.to(dev).requires_grad_(True)
+    out, v_res = psa.psa_attention(x, h, KD)
+    if with_v_grad:
+        torch.autograd.backward([out, v_res], [dout.to(dev), dv.to(dev)])
+    else:
+        out.backward(dout.to(dev))
+    out_ref, v_ref, lse = psa.psa_attention_fwd(qkv.to(dev), h, KD)
+    dx_ref = psa.psa_attention_bwd(qkv.to(dev), out_ref, lse, dout.to(dev), h, KD,
+                                   dv=dv.to(dev) if with_v_grad else None)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), out_ref) and torch.equal(v_res.detach(), v_ref)
+    assert torch.equal(x.grad, dx_ref)
+    want = O.psa_backward(to_f64(qkv), to_f64(dout), to_f64(dv) if with_v_grad else None, B, h, KD, H, W)
+    assert_attention_close(to_f64(x.grad), want, "bf16", "d(qkv) via autograd")

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     fa2_fwd_workspace_bytes,
     load_library,
     psa_abi_version,
+    psa_attention,
     psa_attention_bwd,
     psa_attention_fwd,
     psa_attention_fwd_workspace_bytes,

@@ -253,6 +253,34 @@ def psa_attention_bwd(qkv, out, lse, dout, heads, key_dim, dv=None, scale=None, 
     return dqkv
 
 
+class _PsaAttention(torch.autograd.Function):
+    """Autograd node over the fused PSA forward and its backward (both in libpsa)."""
+
+    @staticmethod
+    def forward(ctx, qkv, heads, key_dim, scale, workspace):
+        out, v_res, lse = psa_attention_fwd(qkv, heads, key_dim, scale=scale, workspace=workspace)
+        ctx.save_for_backward(qkv, out, lse)
+        ctx.heads, ctx.key_dim, ctx.scale = heads, key_dim, scale
+        return out, v_res
+
+    @staticmethod
+    def backward(ctx, dout, dv_res):
+        qkv, out, lse = ctx.saved_tensors
+        if dout is None:
+            dout = torch.zeros_like(out)
+        dqkv = psa_attention_bwd(qkv, out, lse, dout.contiguous(), ctx.heads, ctx.key_dim,
+                                 dv=None if dv_res is None else dv_res.contiguous(), scale=ctx.scale)
+        return dqkv, None, None, None, None
+
+
+def psa_attention(qkv, heads, key_dim, scale=None, workspace=None):
+    """The PSA attention block as a differentiable op: NCHW ``qkv`` -> ``(out, v_residual)``.
+
+    Forward is ``psa_attention_fwd``; the gradient with respect to ``qkv`` (from both outputs)
+    is ``psa_attention_bwd``. bf16 only for the backward (the library's PSA backward)."""
+    return _PsaAttention.apply(qkv, heads, key_dim, scale, workspace)
+
+
 def _f32(t, name, shape=None):
     _dev(t, name)
     if t.dtype != torch.float32:
