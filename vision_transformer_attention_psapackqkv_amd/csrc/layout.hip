@@ -8,10 +8,11 @@
 // [N, KD] matrix. So every op is a batch of [KD, N] <-> [N, KD] transposes
 // with a slab-index permutation, and each is bound by HBM bandwidth.
 //
-// A workgroup moves one tile of a slab (all KD channels x 16 KB / (KD * elt)
-// pixels) through LDS: 16-byte loads along the side the data is contiguous on,
-// the transpose between LDS and registers, 16-byte stores along the other
-// side, so that every wave instruction reads or writes 1 KB of contiguous runs
+// A workgroup (256 threads for pack, 512 for merge and extract) moves one
+// tile of a slab (all KD channels x 16 KB / (KD * elt) pixels) through LDS:
+// 16-byte loads along the side the data is contiguous on, the transpose
+// between LDS and registers, 16-byte stores along the other side, so that
+// every wave instruction reads or writes 1 KB of contiguous runs
 // on both sides (whole channel-row runs on the NCHW side, whole consecutive
 // rows on the packed side). Rows whose start is not 16-byte aligned (N not a
 // multiple of 16 bytes / element size) take a scalar kernel instead. Measured
@@ -54,8 +55,11 @@ __device__ __forceinline__ void slab_offsets(const SlabGeom& g, int t, int64_t& 
 // chunk does not run along. LDS chunk columns are XOR-swizzled by the row's
 // channel block, so the 8 rows (4 for f32) one packed-side chunk gathers from
 // sit in different bank groups.
-constexpr int kThreadsLds = 256;
 constexpr int kTileBytes = 16384;
+// Workgroup size: 256 threads for pack, 512 for merge and extract (measured
+// best for each direction on MI355X at the 80x80 map; 4 and 2 chunks per thread).
+template <bool kToRows>
+constexpr int threads_lds() { return kToRows ? 256 : 512; }
 
 template <int kElt>
 struct Word;
@@ -66,7 +70,7 @@ struct Word<4> { using T = uint32_t; };
 
 // kToRows = true: NCHW [KD, N] slabs -> packed [N, KD] slabs (pack).
 // kToRows = false: packed [N, KD] slabs -> NCHW [KD, N] slabs (merge, extract).
-template <int kElt, int KD, bool kToRows>
+template <int kElt, int KD, bool kToRows, int kThreadsLds = threads_lds<kToRows>()>
 __global__ __launch_bounds__(kThreadsLds) void transpose_slabs_lds(const void* __restrict__ src_v,
                                                                    void* __restrict__ dst_v,
                                                                    SlabGeom g, int tiles_per_slab) {
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(kThreadsLds) void transpose_slabs_lds(const void* _
   constexpr int PX = kTileBytes / (KD * kElt);   // pixels per tile
   constexpr int CPR = PX / VEC;                  // chunks per channel row of a tile (>= 8)
   constexpr int DBN = KD / VEC;                  // chunks per packed row
-  constexpr int PER = KD * CPR / kThreadsLds;    // chunks per thread (4)
+  constexpr int PER = KD * CPR / kThreadsLds;    // chunks per thread
   static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0 && KD * CPR == PER * kThreadsLds, "tile shape");
   __shared__ __attribute__((aligned(16))) T lds[KD * PX];
 
@@ -182,7 +186,7 @@ void launch_lds(const void* src, void* dst, SlabGeom g, int n_slabs, hipStream_t
     constexpr int PX = kTileBytes / (KD * kElt);
     const int tiles = (g.N + PX - 1) / PX;
     const dim3 grid(static_cast<unsigned>(n_slabs) * tiles);
-    transpose_slabs_lds<kElt, KD, kToRows><<<grid, kThreadsLds, 0, stream>>>(src, dst, g, tiles);
+    transpose_slabs_lds<kElt, KD, kToRows><<<grid, threads_lds<kToRows>(), 0, stream>>>(src, dst, g, tiles);
   };
   switch (g.KD) {
     case 16: go(std::integral_constant<int, 16>{}); break;
