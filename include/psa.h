@@ -47,7 +47,15 @@ extern "C" {
 
 #define PSA_ABI_VERSION 3
 
+/* Element type. A C caller may pass any int; the library rejects values other
+ * than these two with PSA_ERR_UNSUPPORTED. Compiled as C++, the enum gets int as
+ * its fixed underlying type (the same size and ABI as the C enum), so that such
+ * a value is a valid psa_dtype there too and the check on it stays meaningful. */
+#ifdef __cplusplus
+typedef enum psa_dtype : int {
+#else
 typedef enum psa_dtype {
+#endif
   PSA_F32 = 0,
   PSA_BF16 = 1
 } psa_dtype;
