@@ -141,7 +141,9 @@ psa_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
  *   dq = scale * dS k,  dk = scale * dS^T q,  dv = P^T dout.
  * q, o, dout, dq: [BH, n_q, head_dim]; k, v, dk, dv: [BH, n_k, head_dim];
  * lse: [BH, n_q] float32 as written by fa2_fwd; workspace: caller-owned
- * float32 scratch of fa2_bwd_workspace_bytes(BH, n_q) bytes (holds Delta).
+ * float32 scratch of fa2_bwd_workspace_bytes(BH, n_q) bytes (the library keeps
+ * -Delta there between its launches; its contents on return are not part of the
+ * results).
  * scale must be the one given to fa2_fwd.
  */
 psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -36,7 +36,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;         // [BH, n_q]
+  float* delta;         // -Delta = -rowsum(dO o), [BH, n_q]
   int BH, n_q, n_k;
   int tiles;            // workgroups per batch-head
   float scale;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 #pragma unroll
     for (int d = 0; d < D; ++d) acc = fmaf(o[d], g[d], acc);
   }
-  a.delta[row] = acc;
+  a.delta[row] = -acc;   // stored negated: the dP accumulators start from it
 }
 
 // ---------------------------------------------------------------- dK / dV (bf16)
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sacc[4 * r4 + e] = 0.0f;
-          pacc[4 * r4 + e] = -dl[e];
+          pacc[4 * r4 + e] = dl[e];   // -Delta
         }
       }
 #pragma unroll
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sacc[r] = 0.0f;
-        pacc[r] = -dl;
+        pacc[r] = dl;   // -Delta
       }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32(BwdArgs a) {
         dp = fmaf(gs[r][d], vr[d], dp);
       }
       const float p = expf(s * a.scale - ls[r]);
-      const float ds = p * (dp - dls[r]);
+      const float ds = p * (dp + dls[r]);   // dls holds -Delta
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         dv[d] = fmaf(p, gs[r][d], dv[d]);
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dq_f32(BwdArgs a) {
         s = fmaf(qr[d], ks[r][d], s);
         dp = fmaf(gr[d], vs[r][d], dp);
       }
-      const float ds = expf(s * a.scale - lse) * (dp - dl);
+      const float ds = expf(s * a.scale - lse) * (dp + dl);   // dl = -Delta
 #pragma unroll
       for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, ks[r][d], dq[d]);
     }

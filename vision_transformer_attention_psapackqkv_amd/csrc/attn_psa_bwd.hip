@@ -52,7 +52,7 @@ struct PsaBwdArgs {
   const uint16_t* dout;   // [BH * DV, N]
   const uint16_t* dvres;  // [BH * DV, N] or null
   const float* lse;       // [BH, N], natural log
-  float* delta;           // [BH, N]
+  float* delta;           // -Delta = -rowsum(dO O) over both halves, [BH, N]
   float* lse2;            // [BH, N]: LSE * log2(e)
   uint16_t* dqkv;         // [BH * 4KD, N]
   int BH, N, tiles;       // tiles: workgroups per batch-head
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void psa_bwd_prep(PsaBwdArgs a) {
   for (int dv = 0; dv < DV; ++dv)
     acc = fmaf(bf16_bits_to_float(o[static_cast<int64_t>(dv) * a.N]),
                bf16_bits_to_float(g[static_cast<int64_t>(dv) * a.N]), acc);
-  a.delta[idx] = acc;
+  a.delta[idx] = -acc;   // stored negated: the dP accumulators start from it
   a.lse2[idx] = a.lse[idx] * kLog2e;
 }
 
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           sacc[8 * h + j] = 0.0f;
-          pacc[8 * h + j] = -(j < 4 ? d0[j] : d1[j - 4]);
+          pacc[8 * h + j] = j < 4 ? d0[j] : d1[j - 4];   // -Delta
         }
       }
 #pragma unroll
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sacc[r] = 0.0f;
-        pacc[r] = -dl;
+        pacc[r] = dl;   // -Delta
       }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds)
