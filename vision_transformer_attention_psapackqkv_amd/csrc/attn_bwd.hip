@@ -5,7 +5,8 @@
 // grid. With P = exp(scale*Q K^T - LSE) recomputed from the forward's LSE,
 // Delta = rowsum(dO * O) and dS = P * (dO V^T - Delta):
 //   dV = P^T dO,   dK = scale * dS^T Q,   dQ = scale * dS K.
-// Three launches: Delta (one pass over O and dO), dK/dV (one workgroup per
+// Three launches: Delta (one pass over O and dO; stored negated, as the dP
+// accumulators start from -Delta), dK/dV (one workgroup per
 // key tile, looping over query tiles) and dQ (one workgroup per query tile,
 // looping over key tiles). Neither uses atomics.
 //

@@ -12,7 +12,7 @@
 //   dV    = P^T dO + dV_residual,   dK = s dS^T Q,   dQ = s dS K.
 // Like the page's FA2 backward, dQ and dK/dV are separate kernels with their
 // own grids (no atomics):
-//   psa_bwd_prep: Delta and LSE * log2(e) per (bh, pixel);
+//   psa_bwd_prep: -Delta and LSE * log2(e) per (bh, pixel);
 //   psa_bwd_dkdv: one workgroup per (bh, 128 keys), looping over 64-query tiles;
 //   psa_bwd_dq:   one workgroup per (bh, 128 queries), looping over 64-key tiles.
 // Every tensor is read and written in NCHW (channel rows of N pixels), so the
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
   constexpr int NDS = KD / 16, NVS = DV / 16;
   constexpr int NDK = DP / 32, NDV = DV / 32;
   constexpr int Q_EL = DP * kTN, DO_EL = DV * kTN;
-  constexpr int BUF = Q_EL + DO_EL + 2 * kTN * 2;   // + LSE*log2(e) and Delta (floats)
+  constexpr int BUF = Q_EL + DO_EL + 2 * kTN * 2;   // + LSE*log2(e) and -Delta (floats)
   // Two tile buffers as two objects reached through restrict pointers, so the
   // LDS reads of one tile need not wait for the direct loads into the other.
   __shared__ __attribute__((aligned(16))) uint16_t smem0[BUF];
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) dv[b][r] = 0.0f;
 
-  // Per query tile: Q rows, dO rows, and (threads 0..127) LSE*log2(e) / Delta.
+  // Per query tile: Q rows, dO rows, and (threads 0..127) LSE*log2(e) / -Delta.
   StageRegs<KD> sq;
   StageRegs<DV> sg;
   float fval = 0.0f;

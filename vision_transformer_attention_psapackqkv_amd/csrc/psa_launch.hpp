@@ -32,12 +32,12 @@ hipError_t launch_psa_fused_fwd(const void* qkv, void* out, void* vres, float* l
 size_t psa_fused_split_bytes(int BH, int KD, int N, bool bf16);
 
 // PSA backward (bf16): qkv, out, dout [, dvres] NCHW + lse -> dqkv NCHW.
-// workspace: 2 * BH * N floats (Delta, LSE * log2(e)).
+// workspace: 2 * BH * N floats (-Delta, LSE * log2(e)).
 hipError_t launch_psa_fused_bwd(const void* qkv, const void* out, const float* lse, const void* dout,
                                 const void* dvres, void* dqkv, float* workspace, int BH, int KD,
                                 int N, float scale, hipStream_t stream);
 
-// FA2 backward: Delta into workspace, then the dK/dV and dQ kernels.
+// FA2 backward: -Delta into the workspace, then the dK/dV and dQ kernels.
 hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
                           float* delta, int BH, int n_q, int n_k, int D, float scale, bool bf16,
