@@ -192,20 +192,26 @@ struct FwdStageDirect {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.k + static_cast<int64_t>(bh) * 4 * KD * N), 0, 4 * KD * N * 2,
         kBufferWord3);
+    if (!last) {   // whole tile: per-lane offsets as set up by init(), tile origin scalar
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int b = wave + i * kWaves;
+        if (BLOCKS % kWaves != 0 && b >= BLOCKS) break;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(buf + b * 512), 16, voff[i],
+            (chan0(b) * N + m0) * 2, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int b = wave + i * kWaves;
-      if (b >= BLOCKS) break;
-      uint32_t vo = voff[i];
-      int so = (chan0(b) * N + m0) * 2;
-      if (last) {
-        int m = m0 + chunk(b, lane) * 8;
-        m = m < N ? m : N - 8;
-        vo = static_cast<uint32_t>((lane >> 3) * N + m) * 2u;
-        so = chan0(b) * N * 2;
-      }
+      if (BLOCKS % kWaves != 0 && b >= BLOCKS) break;
+      int m = m0 + chunk(b, lane) * 8;
+      m = m < N ? m : N - 8;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(buf + b * 512), 16, vo, so, 0, 0);
+          rsrc, (__attribute__((address_space(3))) void*)(buf + b * 512), 16,
+          static_cast<uint32_t>((lane >> 3) * N + m) * 2u, chan0(b) * N * 2, 0, 0);
     }
   }
 };
@@ -267,19 +273,26 @@ struct FwdStagePacked {
         const_cast<uint16_t*>(a.k + base), 0, n * KD * 2, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.v + base), 0, n * KD * 2, kBufferWord3);
+    if (!last) {   // whole tile: per-lane offsets as set up by init(), tile origin scalar
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int b = wave + i * kWaves;
+        if (BLOCKS % kWaves != 0 && b >= BLOCKS) break;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            b < K_BLOCKS ? rk : rv, (__attribute__((address_space(3))) void*)(buf + b * 512), 16, voff[i],
+            m0 * KD * 2, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int b = wave + i * kWaves;
-      if (b >= BLOCKS) break;
-      uint32_t vo = voff[i];
-      if (last) {
-        const int r = row_of(b, lane);
-        const int m = m0 + r < n ? r : n - 1 - m0;
-        vo = static_cast<uint32_t>(m * KD + chunk_of(b, lane) * 8) * 2u;
-      }
+      if (BLOCKS % kWaves != 0 && b >= BLOCKS) break;
+      const int r = row_of(b, lane);
+      const int m = m0 + r < n ? r : n - 1 - m0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b < K_BLOCKS ? rk : rv, (__attribute__((address_space(3))) void*)(buf + b * 512), 16, vo,
-          m0 * KD * 2, 0, 0);
+          b < K_BLOCKS ? rk : rv, (__attribute__((address_space(3))) void*)(buf + b * 512), 16,
+          static_cast<uint32_t>(m * KD + chunk_of(b, lane) * 8) * 2u, m0 * KD * 2, 0, 0);
     }
   }
 };

@@ -103,21 +103,31 @@ __device__ __forceinline__ void stage_direct(const uint16_t* src, int N, int m0,
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, R * N * 2, kBufferWord3);
   const bool last = m0 + kTN > N;
+  if (!last) {
+    // Whole tile: the lane's offset depends on the lane and block only (the
+    // compiler keeps it across tiles); the tile origin goes in the scalar offset.
+#pragma unroll
+    for (int i = 0; i < (BLOCKS + kWavesBwd - 1) / kWavesBwd; ++i) {
+      const int b = wave + i * kWavesBwd;
+      if (BLOCKS % kWavesBwd != 0 && b >= BLOCKS) break;
+      const int r = lane >> 3;
+      const int pos = tile_chunk_pos(b * 8 + r, lane & 7) * 8;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(dst + b * 512), 16,
+          static_cast<uint32_t>(r * N + pos) * 2u, (b * 8 * N + m0) * 2, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < (BLOCKS + kWavesBwd - 1) / kWavesBwd; ++i) {
     const int b = wave + i * kWavesBwd;
-    if (b >= BLOCKS) break;
+    if (BLOCKS % kWavesBwd != 0 && b >= BLOCKS) break;
     const int r = lane >> 3;
     const int pos = tile_chunk_pos(b * 8 + r, lane & 7) * 8;
-    uint32_t vo = static_cast<uint32_t>(r * N + pos) * 2u;
-    int so = (b * 8 * N + m0) * 2;
-    if (last) {
-      const int m = m0 + pos < N ? m0 + pos : N - 8;
-      vo = static_cast<uint32_t>(r * N + m) * 2u;
-      so = b * 8 * N * 2;
-    }
+    const int m = m0 + pos < N ? m0 + pos : N - 8;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(dst + b * 512), 16, vo, so, 0, 0);
+        rsrc, (__attribute__((address_space(3))) void*)(dst + b * 512), 16,
+        static_cast<uint32_t>(r * N + m) * 2u, b * 8 * N * 2, 0, 0);
   }
 }
 
