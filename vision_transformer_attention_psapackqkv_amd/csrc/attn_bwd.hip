@@ -19,6 +19,8 @@
 // (ds_read_b64_tr_b16). Tiles are staged once, as plain padded rows.
 #include <math.h>
 
+#include <type_traits>
+
 #include "psa_device.hpp"
 #include "psa_launch.hpp"
 
@@ -379,7 +381,10 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
   tile.store(smem, tid);
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  // One key tile. Only the last tile (`last` true) can hold keys past n_k,
+  // and only its code masks them: a run-time test on every tile is flattened
+  // by the compiler into a compare and a select per score.
+  auto step = [&](int kt, auto last) __attribute__((always_inline)) {
     const uint16_t* buf = smem + (kt & 1) * Tile::BUF;
     const bool more = kt + 1 < n_tiles;
     if (more) tile.load(a, bh, kt + 1, tid);
@@ -403,8 +408,8 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
         sacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_K + off), qop[ds], sacc);
         pacc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + Tile::OFF_V + off), gop[ds], pacc);
       }
-      // Keys past n_k (last tile only) get P = 0.
-      if ((kt + 1) * BN > a.n_k) {
+      // Keys past n_k get P = 0.
+      if constexpr (decltype(last)::value) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kt * BN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7) >= a.n_k) sacc[r] = -INFINITY;
@@ -433,7 +438,9 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
       }
     if (more) tile.store(smem + ((kt + 1) & 1) * Tile::BUF, tid);
     __syncthreads();
-  }
+  };
+  for (int kt = 0; kt + 1 < n_tiles; ++kt) step(kt, std::false_type{});
+  step(n_tiles - 1, std::true_type{});
 
   if (!q_ok) return;
 #pragma unroll

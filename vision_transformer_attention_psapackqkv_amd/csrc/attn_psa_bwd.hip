@@ -36,6 +36,8 @@
 // otherwise. Scores use base 2: P = 2^(S * s*log2(e) - LSE*log2(e)).
 #include <math.h>
 
+#include <type_traits>
+
 #include "psa_device.hpp"
 #include "psa_launch.hpp"
 
@@ -185,6 +187,7 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
   constexpr int DP = KD < 32 ? 32 : KD;   // Q tile rows (one MFMA block minimum)
   constexpr int NDS = KD / 16, NVS = DV / 16;
   constexpr int NDK = DP / 32, NDV = DV / 32;
+  constexpr int kQbUnroll = KD <= 32 && kVecN ? kTN / 32 : 1;   // query blocks unrolled per tile
   constexpr int Q_EL = DP * kTN, DO_EL = DV * kTN;
   constexpr int BUF = Q_EL + DO_EL + 2 * kTN * 2;   // + LSE*log2(e) and -Delta (floats)
   // Two tile buffers as two objects reached through restrict pointers, so the
@@ -282,8 +285,13 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
     const bool more = qt + 1 < n_tiles;
     if (more) issue(qt + 1, nbuf);
 
-#pragma unroll 1
+    // Up to key_dim 32, with directly staged tiles, the blocks are unrolled
+    // (every LDS address a per-lane offset plus a constant) but kept one after
+    // the other, not interleaved, which would hold both blocks' registers. The
+    // other kernels keep the rolled loop, which spills less or not at all.
+#pragma unroll kQbUnroll
     for (int qb = 0; qb < kTN / 32; ++qb) {
+      if (kQbUnroll > 1 && qb > 0) __builtin_amdgcn_sched_barrier(0);
       // Rows of S and dP: query qb*32 + 16*(r/8) + 8g + r%8 in element r.
       // dP's accumulator starts at -Delta, so it ends as dP - Delta.
       const int col = qb * 32 + 16 * t16 + tr_key_col(i16 & 3);
@@ -446,8 +454,11 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
   finish(smem0);
   __syncthreads();
 
-  // One key tile, read from ks while the next one is loaded into nbuf.
-  auto tile = [&](int kt, const uint16_t* __restrict__ ks, uint16_t* __restrict__ nbuf)
+  // One key tile, read from ks while the next one is loaded into nbuf. Only
+  // the last tile (`last` true) can hold keys past N, and only its code masks
+  // them: a run-time test on every tile is flattened by the compiler into a
+  // compare and a select per score.
+  auto tile = [&](int kt, const uint16_t* __restrict__ ks, uint16_t* __restrict__ nbuf, auto last)
                   __attribute__((always_inline)) {
     const uint16_t* vs_ = ks + K_EL;
     const bool more = kt + 1 < n_tiles;
@@ -471,8 +482,8 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
 #pragma unroll
       for (int vs = 0; vs < NVS; ++vs)
         pacc = mfma32x32x16(tile_read_tr8(vs_, vs * 16 + 8 * g + (i16 >> 2), col), gop[vs], pacc);
-      // Keys past N (last tile only) get P = 0.
-      if ((kt + 1) * kTN > N) {
+      // Keys past N get P = 0.
+      if constexpr (decltype(last)::value) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kt * kTN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7) >= N) sacc[r] = -INFINITY;
@@ -492,9 +503,15 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
     if (more) finish(nbuf);
     __syncthreads();
   };
-  for (int kt = 0; kt < n_tiles; ++kt) {   // tile t lives in smem0 for even t, smem1 for odd
+  // Tile t lives in smem0 for even t, smem1 for odd.
+  for (int kt = 0; kt + 1 < n_tiles; ++kt) {
     const bool odd = kt & 1;
-    tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1);
+    tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1, std::false_type{});
+  }
+  {
+    const int kt = n_tiles - 1;
+    const bool odd = kt & 1;
+    tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1, std::true_type{});
   }
 
   if (!q_ok) return;
