@@ -71,6 +71,7 @@ struct FwdArgs {
   int tail;            // query tiles split into key-range pieces (after them)
   int splits;          // pieces per split tile
   float* part;         // per piece: O^T [DV][BM] (unnormalised), m [BM], l [BM]
+  int vres_wgs;        // > 0: workgroups after the attention ones copy the V residual
 };
 
 // Logical query tiles L = bh * q_tiles + qt in XCD-aware order. Workgroups are
@@ -375,6 +376,36 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   const int N = a.n_k;   // NCHW: n_q == n_k == H*W
   const int n_tiles = (a.n_k + kBN - 1) / kBN;
 
+  // V residual workgroups (NCHW, N a multiple of 8): queued after every
+  // attention workgroup, they run on the slots the grid's last partial round
+  // leaves free. A batch-head's V channels are DV*N contiguous elements on
+  // both sides, so the residual is a plain copy of BH such blocks.
+  if constexpr (kNCHW && kVecN) {
+    const int n_attn = a.full + a.tail * a.splits;
+    if (a.vres_wgs > 0 && static_cast<int>(blockIdx.x) >= n_attn) {
+      const int64_t per_bh = static_cast<int64_t>(DV) * N / 8;   // 16-byte chunks
+      const int64_t total = per_bh * a.BH;
+      const int64_t stride = static_cast<int64_t>(a.vres_wgs) * NT;
+      constexpr int BATCH = 8;
+      for (int64_t c0 = static_cast<int64_t>(blockIdx.x - n_attn) * NT + tid; c0 < total; c0 += stride * BATCH) {
+        u32x4 r[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int64_t c = min(c0 + u * stride, total - 1);
+          const int64_t bh_c = c / per_bh;
+          r[u] = ldg_nt(reinterpret_cast<const u32x4*>(a.v + (bh_c * 4 * KD + 2 * KD) * N + (c - bh_c * per_bh) * 8));
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int64_t c = c0 + u * stride;
+          const int64_t bh_c = c / per_bh;
+          if (c < total) stg_nt(reinterpret_cast<u32x4*>(a.vres + bh_c * DV * N + (c - bh_c * per_bh) * 8), r[u]);
+        }
+      }
+      return;
+    }
+  }
+
   // Work unit: a whole query tile, or key tiles [kt0, kt1) (piece `piece`) of
   // split tile `split`.
   int L, split = -1, piece = 0, kt0 = 0, kt1 = n_tiles;
@@ -425,7 +456,7 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   // batch are unconditional (chunks past the map's last pixel re-read its last
   // chunk; only the stores are guarded), so they are all in flight together.
   if constexpr (kNCHW) {
-    if (a.vres != nullptr && piece == 0) {
+    if (a.vres != nullptr && piece == 0 && a.vres_wgs == 0) {
       const int n0 = qt * BM;
       constexpr int CPR = BM / 8;   // 8-pixel chunks per channel row
       constexpr int TOTAL = DV * CPR;
@@ -841,8 +872,10 @@ int tail_splits(int total, int slots, int n_tiles, int& rem) {
 
 // Query tiles, split plan and the workspace bytes the split needs for one
 // launch of attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc> on the current device.
+constexpr int kMinVresWgs = 64;
+
 struct FwdPlan {
-  int q_tiles, full, tail, splits;
+  int q_tiles, full, tail, splits, slots;
   size_t bytes;
 };
 
@@ -860,7 +893,8 @@ FwdPlan plan_bf16(int BH, int n_q, int n_k) {
   p.q_tiles = (n_q + C::BM - 1) / C::BM;
   const int total = BH * p.q_tiles;
   int rem = 0;
-  p.splits = tail_splits(total, occ * cu_count(), (n_k + kBN - 1) / kBN, rem);
+  p.slots = occ * cu_count();
+  p.splits = tail_splits(total, p.slots, (n_k + kBN - 1) / kBN, rem);
   p.tail = rem;
   p.full = total - rem;
   p.bytes = sizeof(float) * static_cast<size_t>(C::PART) * rem * p.splits;
@@ -882,8 +916,19 @@ hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream)
   a.tail = p.tail;
   a.splits = p.splits;
   a.part = static_cast<float*>(ws);
+  // When the tail is split, its pieces leave HBM mostly idle: the V residual
+  // then goes to extra workgroups on the slots the last round leaves free (at
+  // least kMinVresWgs of them). Otherwise each workgroup copies its own
+  // pixels' V channels before its key loop (copy workgroups beside a last
+  // round of whole query tiles measured slower).
+  const int n_attn = p.full + p.tail * p.splits;
+  a.vres_wgs = 0;
+  if (kNCHW && kVecN && a.vres != nullptr && p.tail > 0 && p.slots > 0) {
+    const int last = n_attn % p.slots;
+    if (last != 0 && p.slots - last >= kMinVresWgs) a.vres_wgs = p.slots - last;
+  }
   attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>
-      <<<dim3(static_cast<unsigned>(p.full + p.tail * p.splits)), C::NT, 0, stream>>>(a);
+      <<<dim3(static_cast<unsigned>(n_attn + a.vres_wgs)), C::NT, 0, stream>>>(a);
   if (p.tail > 0) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
