@@ -178,9 +178,9 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1. (Every batch-head is "
-              "an independent problem, so several GPUs would each run this same kernel on their "
-              "share of the batch with no exchange; that mode is not built here.)", file=sys.stderr)
+        print("bench.py: runs on one GPU only; --gpus must be 1. (Every batch-head is an "
+              "independent problem, so several GPUs would each run this same kernel on their "
+              "share of the batch with no exchange; that mode is not implemented.)", file=sys.stderr)
         sys.exit(2)
 
     import torch
