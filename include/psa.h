@@ -6,8 +6,8 @@
  * channels are grouped per head as [Q | K | V_lo | V_hi] (each KEY_DIM wide),
  * is repacked to [4, BH, N, KEY_DIM]; Flash Attention 2 runs once per V half
  * with HEAD_DIM = KEY_DIM, sharing Q and K; the two outputs are merged back to
- * NCHW [B, c, H, W]; the V section is also written back out in NCHW for the
- * residual path. psa_attention_fwd does all of it in one kernel.
+ * NCHW [B, c, H, W]; the two V halves are also returned to NCHW, where the
+ * block's residual branch uses them. psa_attention_fwd does all of it in one kernel.
  *
  * Notation: h = heads, KD = key_dim, N = H*W, BH = B*h, n = y*W + x,
  * bh = b*h + i (head i of batch item b), qkv_h = 4*h*KD, c = 2*h*KD.

@@ -11,8 +11,8 @@ What it follows (all citations are to the pages the method is described on):
   (PSA)": PsaPackQkv takes the NCHW output ``[B, qkv_h, H, W]`` of a QKV
   convolution whose channels are grouped per head as ``[Q | K | V_lo | V_hi]``,
   each KEY_DIM wide, and produces the ``[4, BH, N, KEY_DIM]`` layout Flash
-  Attention 2 reads; PsaExtractV pulls the V section back out in NCHW for the
-  residual path; PsaMergeAttn writes the attention output back to NCHW
+  Attention 2 reads; PsaExtractV returns the two V sections to NCHW, where the
+  block's residual branch uses them; PsaMergeAttn writes the attention output back to NCHW
   ``[B, c, H, W]``. Flash Attention 2 runs once per V half with
   HEAD_DIM = KEY_DIM, sharing Q and K.
 * same page, section "Flash Attention 2": standard FA2 over

@@ -252,3 +252,22 @@ def test_ciou_argument_errors():
     p = list(bwd)
     p[6] = p[5]                           # dpred aliases dloss
     assert call_b(p)[0] == 5
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipGetErrorString.restype = ctypes.c_char_p
+    return lib
+
+
+def test_rejected_call_leaves_a_stale_hip_error_alone():
+    """A HIP error left by an earlier, unrelated call on this thread: an entry point that rejects
+    its arguments launches nothing, reports its own validation failure and leaves that error for
+    the caller to read. (That a launching entry point clears such an error first, so it is not
+    reported as the entry point's launch failure, needs a GPU: tests/test_layout_gpu.py.)"""
+    hip = _hip()
+    stale = hip.hipSetDevice(9999)
+    assert stale != 0
+    st, msg = _status("psa_pack_qkv", A, B_, 2, 2, 24, 4, 4, 1, None)
+    assert st == 3 and msg == "psa_pack_qkv: key_dim=24 is not one of 16, 32, 64, 128"
+    assert hip.hipGetLastError() == stale

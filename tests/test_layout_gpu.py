@@ -92,3 +92,21 @@ def test_full_size_bit_exact(name):
     assert np.array_equal(bits(v), O.extract_v(want, w.B, w.heads, w.key_dim, w.H, w.W))
     merged = psa.psa_merge_attn(packed[:2].contiguous(), w.B, w.heads, w.key_dim, w.H, w.W)
     assert np.array_equal(bits(merged), O.merge_attn(want[:2], w.B, w.heads, w.key_dim, w.H, w.W))
+
+
+def test_stale_hip_error_is_not_reported_as_a_launch_failure():
+    """A HIP error left on this thread by an earlier, unrelated call (here hipSetDevice on a
+    device that does not exist) must not come back as an entry point's PSA_ERR_LAUNCH: the entry
+    point clears it before its launches, which then succeed."""
+    import ctypes
+    dev = device()
+    hip = ctypes.CDLL("libamdhip64.so")
+    B, h, KD, H, W = 1, 2, 32, 4, 4
+    qkv = I.make_qkv(B, h, KD, H, W, dtype="bf16", seed=5)
+    x = qkv.to(dev)
+    torch.cuda.synchronize()
+    announce("psa_pack_qkv after a stale hipSetDevice(9999) error")
+    assert hip.hipSetDevice(9999) != 0
+    packed = psa.psa_pack_qkv(x, h, KD)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(packed), O.pack_qkv(bits(qkv), B, h, KD, H, W))

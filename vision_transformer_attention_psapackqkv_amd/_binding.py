@@ -89,6 +89,42 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _arg(t, name: str, shape=None, dtype=None, like: torch.Tensor | None = None, min_bytes=None):
+    """Checks a tensor handed to the C ABI against the sizes the call will use: its shape and
+    dtype (where given), at least ``min_bytes`` bytes (a workspace), a GPU tensor on ``like``'s
+    device, contiguous. Raises ValueError before anything is allocated or launched: the kernels
+    trust these sizes, so a wrong one would read or write past the tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {min_bytes}")
+    _dev(t, name)
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+    return t
+
+
+def _float_dtype(t: torch.Tensor, name: str):
+    if t.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"{name} has dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+    return t.dtype
+
+
+def _nchw(qkv, heads, key_dim, name="qkv"):
+    """(B, H, W) of an NCHW qkv tensor ``[B, 4*heads*key_dim, H, W]``."""
+    if not isinstance(qkv, torch.Tensor) or qkv.dim() != 4:
+        raise ValueError(f"{name} must be a 4-D NCHW tensor")
+    B, C, H, W = qkv.shape
+    if C != 4 * heads * key_dim:
+        raise ValueError(f"{name} has {C} channels, expected 4*heads*key_dim = {4 * heads * key_dim}")
+    _float_dtype(qkv, name)
+    return B, H, W
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -103,25 +139,26 @@ def default_scale(key_dim: int) -> float:
 
 def psa_pack_qkv(qkv: torch.Tensor, heads: int, key_dim: int, out: torch.Tensor | None = None):
     """qkv NCHW ``[B, 4*heads*key_dim, H, W]`` -> packed ``[4, B*heads, H*W, key_dim]``."""
-    _dev(qkv, "qkv")
-    B, C, H, W = qkv.shape
-    if C != 4 * heads * key_dim:
-        raise ValueError(f"qkv has {C} channels, expected 4*heads*key_dim = {4 * heads * key_dim}")
+    B, H, W = _nchw(qkv, heads, key_dim)
+    _arg(qkv, "qkv")
+    shape = (4, B * heads, H * W, key_dim)
     if out is None:
-        out = torch.empty((4, B * heads, H * W, key_dim), dtype=qkv.dtype, device=qkv.device)
-    _check(load_library().psa_pack_qkv(qkv.data_ptr(), _dev(out, "out").data_ptr(), B, heads,
+        out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device)
+    _arg(out, "out", shape, qkv.dtype, like=qkv)
+    _check(load_library().psa_pack_qkv(qkv.data_ptr(), out.data_ptr(), B, heads,
                                        key_dim, H, W, _dtype_code(qkv), _stream(qkv)))
     return out
 
 
 def _rows_to_nchw(fn_name, rows, slots, B, heads, key_dim, H, W, out):
-    _dev(rows, "input")
-    if tuple(rows.shape) != (slots, B * heads, H * W, key_dim):
-        raise ValueError(f"input shape {tuple(rows.shape)} != {(slots, B * heads, H * W, key_dim)}")
+    _arg(rows, "input", (slots, B * heads, H * W, key_dim))
+    _float_dtype(rows, "input")
+    shape = (B, 2 * heads * key_dim, H, W)
     if out is None:
-        out = torch.empty((B, 2 * heads * key_dim, H, W), dtype=rows.dtype, device=rows.device)
+        out = torch.empty(shape, dtype=rows.dtype, device=rows.device)
+    _arg(out, "out", shape, rows.dtype, like=rows)
     fn = getattr(load_library(), fn_name)
-    _check(fn(rows.data_ptr(), _dev(out, "out").data_ptr(), B, heads, key_dim, H, W,
+    _check(fn(rows.data_ptr(), out.data_ptr(), B, heads, key_dim, H, W,
               _dtype_code(rows), _stream(rows)))
     return out
 
@@ -136,14 +173,14 @@ def psa_merge_attn(o2, B, heads, key_dim, H, W, out=None):
     return _rows_to_nchw("psa_merge_attn", o2, 2, B, heads, key_dim, H, W, out)
 
 
-def _workspace(ws, nbytes, device):
+def _workspace(ws, nbytes, like):
     """(pointer, bytes) of a forward workspace: a new one of ``nbytes`` if ``ws`` is None,
-    else the given tensor (an empty one runs the launch unsplit)."""
+    else the given tensor, of any size (a smaller or empty one runs the launch unsplit)."""
     if ws is None:
         if nbytes == 0:
             return None, 0
-        ws = torch.empty((nbytes,), dtype=torch.uint8, device=device)
-    _dev(ws, "workspace")
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device=like.device)
+    _arg(ws, "workspace", like=like)
     return (ws.data_ptr() if ws.numel() else None), ws.numel() * ws.element_size()
 
 
@@ -159,40 +196,58 @@ def psa_attention_fwd_workspace_bytes(B, heads, key_dim, H, W, dtype=torch.bfloa
     return load_library().psa_attention_fwd_workspace_bytes(B, heads, key_dim, H, W, code)
 
 
+def _qkv3(q, k, v):
+    """(BH, n_q, D, n_k) of FA2's ``[BH, n, D]`` q, k, v (k and v share q's BH, D and dtype)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-D [BH, n_q, D] tensor")
+    _float_dtype(q, "q")
+    _arg(q, "q")
+    BH, n_q, D = q.shape
+    if not isinstance(k, torch.Tensor) or k.dim() != 3:
+        raise ValueError("k must be a 3-D [BH, n_k, D] tensor")
+    n_k = k.shape[1]
+    _arg(k, "k", (BH, n_k, D), q.dtype, like=q)
+    _arg(v, "v", (BH, n_k, D), q.dtype, like=q)
+    return BH, n_q, D, n_k
+
+
 def fa2_fwd(q, k, v, scale=None, out=None, lse=None, want_lse=True, workspace=None):
     """FA2 forward on ``[BH, n, D]`` tensors; returns ``(o, lse)`` (lse is None if not wanted).
 
     ``workspace``: None allocates the bytes ``fa2_fwd_workspace_bytes`` asks for; a given
     GPU tensor is used as is (an empty one runs the launch without the tail split)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
-    BH, n_q, D = q.shape
-    n_k = k.shape[1]
-    if tuple(k.shape) != (BH, n_k, D) or tuple(v.shape) != (BH, n_k, D):
-        raise ValueError("k and v must be [BH, n_k, D] with q's BH and D")
+    BH, n_q, D, n_k = _qkv3(q, k, v)
     if out is None:
         out = torch.empty_like(q)
+    _arg(out, "out", q.shape, q.dtype, like=q)
     if lse is None and want_lse:
         lse = torch.empty((BH, n_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _arg(lse, "lse", (BH, n_q), torch.float32, like=q)
     s = default_scale(D) if scale is None else float(scale)
     lib = load_library()
     code = _dtype_code(q)
-    wp, wb = _workspace(workspace, lib.fa2_fwd_workspace_bytes(BH, n_q, n_k, D, code), q.device)
-    _check(lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dev(out, "out").data_ptr(),
+    wp, wb = _workspace(workspace, lib.fa2_fwd_workspace_bytes(BH, n_q, n_k, D, code), q)
+    _check(lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                        _ptr(lse), BH, n_q, n_k, D, s, code, wp, wb, _stream(q)))
     return out, lse
 
 
 def fa2_bwd(q, k, v, o, dout, lse, scale=None, workspace=None):
-    """FA2 backward; returns ``(dq, dk, dv)``."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse")):
-        _dev(t, n)
-    BH, n_q, D = q.shape
-    n_k = k.shape[1]
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    """FA2 backward; returns ``(dq, dk, dv)``.
+
+    ``workspace``: a GPU tensor of at least ``fa2_bwd_workspace_bytes(BH, n_q)`` bytes
+    (BH * n_q floats), or None to allocate one."""
+    BH, n_q, D, n_k = _qkv3(q, k, v)
+    _arg(o, "o", q.shape, q.dtype, like=q)
+    _arg(dout, "dout", q.shape, q.dtype, like=q)
+    _arg(lse, "lse", (BH, n_q), torch.float32, like=q)
     lib = load_library()
+    nbytes = lib.fa2_bwd_workspace_bytes(BH, n_q)
+    if workspace is not None:
+        _arg(workspace, "workspace", min_bytes=nbytes, like=q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
-        nbytes = lib.fa2_bwd_workspace_bytes(BH, n_q)
         workspace = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=q.device)
     s = default_scale(D) if scale is None else float(scale)
     _check(lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
@@ -206,23 +261,26 @@ def psa_attention_fwd(qkv, heads, key_dim, scale=None, want_v=True, want_lse=Tru
     """Fused PSA forward on NCHW ``qkv``; returns ``(out, v_residual, lse)`` (None where not wanted).
 
     ``workspace`` as for :func:`fa2_fwd` (bytes from ``psa_attention_fwd_workspace_bytes``)."""
-    _dev(qkv, "qkv")
-    B, C, H, W = qkv.shape
-    if C != 4 * heads * key_dim:
-        raise ValueError(f"qkv has {C} channels, expected 4*heads*key_dim = {4 * heads * key_dim}")
+    B, H, W = _nchw(qkv, heads, key_dim)
+    _arg(qkv, "qkv")
     shape = (B, 2 * heads * key_dim, H, W)
     if out is None:
         out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device)
+    _arg(out, "out", shape, qkv.dtype, like=qkv)
     if v_out is None and want_v:
         v_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device)
+    if v_out is not None:
+        _arg(v_out, "v_out", shape, qkv.dtype, like=qkv)
     if lse is None and want_lse:
         lse = torch.empty((B * heads, H * W), dtype=torch.float32, device=qkv.device)
+    if lse is not None:
+        _arg(lse, "lse", (B * heads, H * W), torch.float32, like=qkv)
     s = default_scale(key_dim) if scale is None else float(scale)
     lib = load_library()
     code = _dtype_code(qkv)
     wp, wb = _workspace(workspace, lib.psa_attention_fwd_workspace_bytes(B, heads, key_dim, H, W, code),
-                        qkv.device)
-    _check(lib.psa_attention_fwd(qkv.data_ptr(), _dev(out, "out").data_ptr(), _ptr(v_out),
+                        qkv)
+    _check(lib.psa_attention_fwd(qkv.data_ptr(), out.data_ptr(), _ptr(v_out),
                                  _ptr(lse), B, heads, key_dim, H, W, s, code, wp, wb, _stream(qkv)))
     return out, v_out, lse
 
@@ -232,23 +290,29 @@ def psa_attention_bwd(qkv, out, lse, dout, heads, key_dim, dv=None, scale=None, 
     """PSA backward: the gradient of ``psa_attention_fwd``'s outputs with respect to ``qkv``.
 
     ``out`` and ``lse`` are the forward's, ``dout`` the gradient of ``out``, ``dv`` the gradient
-    of the V residual (None: none). Returns ``dqkv`` NCHW ``[B, 4*heads*key_dim, H, W]``."""
-    for t, n in ((qkv, "qkv"), (out, "out"), (lse, "lse"), (dout, "dout")):
-        _dev(t, n)
+    of the V residual (None: none). Returns ``dqkv`` NCHW ``[B, 4*heads*key_dim, H, W]``.
+    ``workspace``: a GPU tensor of at least ``psa_attention_bwd_workspace_bytes`` bytes, or None."""
+    B, H, W = _nchw(qkv, heads, key_dim)
+    _arg(qkv, "qkv")
+    shape = (B, 2 * heads * key_dim, H, W)
+    _arg(out, "out", shape, qkv.dtype, like=qkv)
+    _arg(lse, "lse", (B * heads, H * W), torch.float32, like=qkv)
+    _arg(dout, "dout", shape, qkv.dtype, like=qkv)
     if dv is not None:
-        _dev(dv, "dv")
-    B, C, H, W = qkv.shape
-    if C != 4 * heads * key_dim:
-        raise ValueError(f"qkv has {C} channels, expected 4*heads*key_dim = {4 * heads * key_dim}")
+        _arg(dv, "dv", shape, qkv.dtype, like=qkv)
+    if dqkv is not None:
+        _arg(dqkv, "dqkv", qkv.shape, qkv.dtype, like=qkv)
     lib = load_library()
+    nbytes = lib.psa_attention_bwd_workspace_bytes(B, heads, H, W)
+    if workspace is not None:
+        _arg(workspace, "workspace", min_bytes=nbytes, like=qkv)
     if dqkv is None:
         dqkv = torch.empty_like(qkv)
     if workspace is None:
-        nbytes = lib.psa_attention_bwd_workspace_bytes(B, heads, H, W)
         workspace = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=qkv.device)
     s = default_scale(key_dim) if scale is None else float(scale)
     _check(lib.psa_attention_bwd(qkv.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                                 _ptr(dv), _dev(dqkv, "dqkv").data_ptr(), _dev(workspace, "workspace").data_ptr(),
+                                 _ptr(dv), dqkv.data_ptr(), workspace.data_ptr(),
                                  B, heads, key_dim, H, W, s, _dtype_code(qkv), _stream(qkv)))
     return dqkv
 

@@ -45,6 +45,7 @@
 // product and the row sum adds the same rounded values.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "psa_device.hpp"
@@ -840,16 +841,16 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
 
 // ------------------------------------------------------------------ dispatch
 
-// Compute units of the current device (0 if unknown).
+// Compute units of the current device (0 if unknown). The per-device cache is
+// atomic: threads that fill it at the same time all store the same value.
 int cu_count() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cus[dev] = n;
-  }
-  return cus[dev];
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    cus[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // Pieces per tail tile. With `slots` workgroups resident at once, `total`
@@ -882,12 +883,16 @@ struct FwdPlan {
 template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
 FwdPlan plan_bf16(int BH, int n_q, int n_k) {
   using C = FwdCfg<KD, DV, kNCHW, kWaves, direct_staging<KD, kNCHW, kVecN>()>;
-  static int occ = -1;   // resident workgroups per CU (the same on every gfx950)
+  // Resident workgroups per CU (the same on every gfx950), cached atomically:
+  // threads that fill the cache at the same time all store the same value.
+  static std::atomic<int> occ_cache{-1};
+  int occ = occ_cache.load(std::memory_order_relaxed);
   if (occ < 0) {
     int n = 0;
     occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(
               &n, reinterpret_cast<const void*>(attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>),
               C::NT, 0) == hipSuccess ? n : 0;
+    occ_cache.store(occ, std::memory_order_relaxed);
   }
   FwdPlan p;
   p.q_tiles = (n_q + C::BM - 1) / C::BM;

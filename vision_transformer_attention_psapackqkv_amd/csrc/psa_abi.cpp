@@ -91,7 +91,16 @@ constexpr int64_t kMaxLanes = (int64_t(1) << 31) - 256;
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-psa_status launched(const char* fn, hipError_t e) {
+// Runs an entry point's launches. HIP keeps one "last error" per thread, set
+// by any earlier failing HIP call and returned (and cleared) by the next
+// hipGetLastError(); the launchers report their launches with that call. It is
+// cleared first, so that a failure left behind by an unrelated earlier call is
+// not reported as this entry point's launch failure. (An error that poisons the
+// device stays sticky and is still reported.)
+template <typename Launch>
+psa_status launched(const char* fn, Launch&& launch) {
+  (void)hipGetLastError();
+  const hipError_t e = launch();
   if (e != hipSuccess) return fail(PSA_ERR_LAUNCH, fn, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -156,24 +165,30 @@ psa_status psa_pack_qkv(const void* qkv_nchw, void* packed, int B, int heads, in
                         int W, psa_dtype dtype, void* stream) {
   const char* fn = "psa_pack_qkv";
   PSA_TRY(layout_entry(fn, qkv_nchw, packed, B, heads, key_dim, H, W, dtype, 4, 4));
-  return launched(fn, psa::launch_pack_qkv(qkv_nchw, packed, B * heads, key_dim, H * W,
-                                           elt_bytes(dtype), as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_pack_qkv(qkv_nchw, packed, B * heads, key_dim, H * W, elt_bytes(dtype),
+                                as_stream(stream));
+  });
 }
 
 psa_status psa_extract_v(const void* packed, void* v_nchw, int B, int heads, int key_dim, int H,
                          int W, psa_dtype dtype, void* stream) {
   const char* fn = "psa_extract_v";
   PSA_TRY(layout_entry(fn, packed, v_nchw, B, heads, key_dim, H, W, dtype, 4, 2));
-  return launched(fn, psa::launch_rows_to_nchw(packed, v_nchw, B * heads, key_dim, H * W, 2,
-                                               elt_bytes(dtype), as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_rows_to_nchw(packed, v_nchw, B * heads, key_dim, H * W, 2, elt_bytes(dtype),
+                                    as_stream(stream));
+  });
 }
 
 psa_status psa_merge_attn(const void* o2, void* out_nchw, int B, int heads, int key_dim, int H,
                           int W, psa_dtype dtype, void* stream) {
   const char* fn = "psa_merge_attn";
   PSA_TRY(layout_entry(fn, o2, out_nchw, B, heads, key_dim, H, W, dtype, 2, 2));
-  return launched(fn, psa::launch_rows_to_nchw(o2, out_nchw, B * heads, key_dim, H * W, 0,
-                                               elt_bytes(dtype), as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_rows_to_nchw(o2, out_nchw, B * heads, key_dim, H * W, 0, elt_bytes(dtype),
+                                    as_stream(stream));
+  });
 }
 
 size_t fa2_fwd_workspace_bytes(int BH, int n_q, int n_k, int head_dim, psa_dtype dtype) {
@@ -206,9 +221,10 @@ psa_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
       PSA_TRY(check_disjoint(fn, pair, 2));
     }
   PSA_TRY(check_disjoint(fn, outs, 3));
-  return launched(fn, psa::launch_fa2_fwd(q, k, v, o, lse, BH, n_q, n_k, head_dim, scale,
-                                          dtype == PSA_BF16, workspace,
-                                          workspace ? workspace_bytes : 0, as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_fa2_fwd(q, k, v, o, lse, BH, n_q, n_k, head_dim, scale, dtype == PSA_BF16,
+                               workspace, workspace ? workspace_bytes : 0, as_stream(stream));
+  });
 }
 
 size_t fa2_bwd_workspace_bytes(int BH, int n_q) {
@@ -241,9 +257,10 @@ psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
       const Range pair[2] = {a, b};
       PSA_TRY(check_disjoint(fn, pair, 2));
     }
-  return launched(fn, psa::launch_fa2_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, BH, n_q,
-                                          n_k, head_dim, scale, dtype == PSA_BF16,
-                                          as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_fa2_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, BH, n_q, n_k, head_dim,
+                               scale, dtype == PSA_BF16, as_stream(stream));
+  });
 }
 
 size_t psa_attention_fwd_workspace_bytes(int B, int heads, int key_dim, int H, int W,
@@ -280,10 +297,11 @@ psa_status psa_attention_fwd(const void* qkv_nchw, void* out_nchw, void* v_nchw,
                       range("lse", lse, lse ? static_cast<int64_t>(B) * heads * H * W : 0, 4),
                       range("workspace", workspace, workspace ? static_cast<int64_t>(workspace_bytes) : 0, 1)};
   PSA_TRY(check_disjoint(fn, r, 5));
-  return launched(fn, psa::launch_psa_fused_fwd(qkv_nchw, out_nchw, v_nchw, lse, B * heads,
-                                                key_dim, H * W, scale, dtype == PSA_BF16, workspace,
-                                                workspace ? workspace_bytes : 0,
-                                                as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_psa_fused_fwd(qkv_nchw, out_nchw, v_nchw, lse, B * heads, key_dim, H * W,
+                                     scale, dtype == PSA_BF16, workspace, workspace ?
+                                     workspace_bytes : 0, as_stream(stream));
+  });
 }
 
 size_t psa_attention_bwd_workspace_bytes(int B, int heads, int H, int W) {
@@ -323,9 +341,10 @@ psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const f
       const Range pair[2] = {a, b};
       PSA_TRY(check_disjoint(fn, pair, 2));
     }
-  return launched(fn, psa::launch_psa_fused_bwd(qkv_nchw, out_nchw, lse, dout_nchw, dv_nchw,
-                                                dqkv_nchw, workspace, B * heads, key_dim, H * W,
-                                                scale, as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_psa_fused_bwd(qkv_nchw, out_nchw, lse, dout_nchw, dv_nchw, dqkv_nchw,
+                                     workspace, B * heads, key_dim, H * W, scale, as_stream(stream));
+  });
 }
 
 psa_status detect_decode(const void* boxes, const float* anchor_x, const float* anchor_y,
@@ -352,8 +371,10 @@ psa_status detect_decode(const void* boxes, const float* anchor_x, const float* 
                       range("anchor_y", anchor_y, A, 4), range("strides", strides, A, 4),
                       range("out", out, n, elt_bytes(dtype))};
   PSA_TRY(check_outputs_disjoint(fn, r, 5, 4));
-  return launched(fn, psa::launch_detect_decode(boxes, anchor_x, anchor_y, strides, out, B, A,
-                                                dtype == PSA_BF16, as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_detect_decode(boxes, anchor_x, anchor_y, strides, out, B, A, dtype ==
+                                     PSA_BF16, as_stream(stream));
+  });
 }
 
 psa_status ciou_loss_fwd(const float* pred, const float* target, float* loss, float* iou,
@@ -370,7 +391,9 @@ psa_status ciou_loss_fwd(const float* pred, const float* target, float* loss, fl
                       range("loss", loss, N, 4),     range("iou", iou, N, 4),
                       range("v", v, N, 4),           range("alpha", alpha, N, 4)};
   PSA_TRY(check_outputs_disjoint(fn, r, 6, 2));
-  return launched(fn, psa::launch_ciou_fwd(pred, target, loss, iou, v, alpha, N, as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_ciou_fwd(pred, target, loss, iou, v, alpha, N, as_stream(stream));
+  });
 }
 
 psa_status ciou_loss_bwd(const float* pred, const float* target, const float* iou,
@@ -389,8 +412,9 @@ psa_status ciou_loss_bwd(const float* pred, const float* target, const float* io
                       range("alpha", alpha, N, 4),     range("dloss", dloss, N, 4),
                       range("dpred", dpred, 4 * N, 4)};
   PSA_TRY(check_outputs_disjoint(fn, r, 7, 6));
-  return launched(fn, psa::launch_ciou_bwd(pred, target, iou, v, alpha, dloss, dpred, N,
-                                           as_stream(stream)));
+  return launched(fn, [&] {
+    return psa::launch_ciou_bwd(pred, target, iou, v, alpha, dloss, dpred, N, as_stream(stream));
+  });
 }
 
 const char* psa_last_error(void) { return g_last_error.c_str(); }
