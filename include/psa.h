@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PSA_ABI_VERSION 3
+#define PSA_ABI_VERSION 4
 
 /* Element type. A C caller may pass any int; the library rejects values other
  * than these two with PSA_ERR_UNSUPPORTED. Compiled as C++, the enum gets int as
@@ -153,6 +153,27 @@ psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
 
 /* Bytes of workspace fa2_bwd needs: BH * n_q floats. 0 if a size is invalid. */
 size_t fa2_bwd_workspace_bytes(int BH, int n_q);
+
+/*
+ * fa2_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc):
+ * the same computation, results bit-identical to fa2_bwd's, with no workspace
+ * argument. The -Delta rows live instead in a scratch array of
+ * PSA_NOALLOC_SCRATCH_BYTES that the library's code object holds in device
+ * memory; each GPU it runs on has its own copy, held until the process ends.
+ * The entry point calls no allocating routine. Limit: BH * n_q <=
+ * PSA_NOALLOC_SCRATCH_BYTES / 4 (4,194,304 rows); larger calls return
+ * PSA_ERR_SHAPE before anything is launched (use fa2_bwd with a workspace).
+ * Every call on one GPU shares that scratch: calls whose executions overlap
+ * on one GPU (on different streams, or from several host threads without
+ * ordering) race and give wrong results; calls ordered on one stream do not.
+ * Other arguments, layouts and errors as fa2_bwd.
+ */
+#define PSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+psa_status fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int BH, int n_q, int n_k, int head_dim, float scale, psa_dtype dtype,
+                           void* stream);
 
 /*
  * The whole PSA forward in one kernel: PsaPackQkv, FA2 over (Q, K, V_lo) and

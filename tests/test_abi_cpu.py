@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     assert names == set(_binding.SIGNATURES), names ^ set(_binding.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.psa_abi_version() == 3
+    assert lib.psa_abi_version() == 4
 
 
 def _status(fn, *args):
@@ -271,3 +271,24 @@ def test_rejected_call_leaves_a_stale_hip_error_alone():
     st, msg = _status("psa_pack_qkv", A, B_, 2, 2, 24, 4, 4, 1, None)
     assert st == 3 and msg == "psa_pack_qkv: key_dim=24 is not one of 16, 32, 64, 128"
     assert hip.hipGetLastError() == stale
+
+
+def test_fa2_bwd_noalloc_argument_errors():
+    """The allocation-free FA2 backward: same argument checks as fa2_bwd, no workspace, and a
+    call larger than the library's scratch is rejected before anything is launched."""
+    p = [A + i * 0x100000 for i in range(9)]
+
+    def call(ptrs=p, BH=4, n_q=64, n_k=64, D=32, scale=0.125, dt=1):
+        return _status("fa2_bwd_noalloc", *ptrs, BH, n_q, n_k, D, scale, dt, None)
+
+    st, msg = call(ptrs=p[:8] + [None])
+    assert st == 1 and msg == "fa2_bwd_noalloc: every pointer argument is required"
+    st, msg = call(D=48)
+    assert st == 3 and "head_dim=48" in msg
+    st, msg = call(BH=0)
+    assert st == 2 and msg.startswith("fa2_bwd_noalloc:")
+    limit = (16 << 20) // 4
+    st, msg = call(BH=2, n_q=limit // 2 + 1, n_k=8)
+    assert st == 2 and "scratch" in msg and str(16 << 20) in msg, msg
+    st, msg = call(ptrs=p[:6] + [p[0]] + p[7:])
+    assert st == 5 and "overlap" in msg

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     detect_decode,
     default_scale,
     fa2_bwd,
+    fa2_bwd_noalloc,
     fa2_fwd,
     fa2_fwd_workspace_bytes,
     load_library,

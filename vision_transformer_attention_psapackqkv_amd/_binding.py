@@ -29,6 +29,7 @@ SIGNATURES = {
     "fa2_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]),
     "fa2_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "fa2_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+    "fa2_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "psa_attention_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]),
     "psa_attention_fwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "psa_attention_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -253,6 +254,31 @@ def fa2_bwd(q, k, v, o, dout, lse, scale=None, workspace=None):
     _check(lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                        workspace.data_ptr(), BH, n_q, n_k, D, s, _dtype_code(q), _stream(q)))
+    return dq, dk, dv
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # PSA_NOALLOC_SCRATCH_BYTES of include/psa.h
+
+
+def fa2_bwd_noalloc(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None):
+    """FA2 backward through ``fa2_bwd_noalloc``: no workspace, the library keeps -Delta in its
+    own device scratch (BH * n_q <= NOALLOC_SCRATCH_BYTES / 4). Returns ``(dq, dk, dv)``; pass
+    them in to have nothing allocated at all. Calls that overlap on one GPU share that scratch
+    and race; calls ordered on one stream do not."""
+    BH, n_q, D, n_k = _qkv3(q, k, v)
+    _arg(o, "o", q.shape, q.dtype, like=q)
+    _arg(dout, "dout", q.shape, q.dtype, like=q)
+    _arg(lse, "lse", (BH, n_q), torch.float32, like=q)
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        if t is not None:
+            _arg(t, n, ref.shape, ref.dtype, like=q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    s = default_scale(D) if scale is None else float(scale)
+    _check(load_library().fa2_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                          dv.data_ptr(), BH, n_q, n_k, D, s, _dtype_code(q), _stream(q)))
     return dq, dk, dv
 
 

@@ -19,6 +19,8 @@
 // (ds_read_b64_tr_b16). Tiles are staged once, as plain padded rows.
 #include <math.h>
 
+#include <mutex>
+
 #include <type_traits>
 
 #include "psa_device.hpp"
@@ -600,6 +602,43 @@ hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of fa2_bwd_noalloc: the -Delta rows the dK/dV and dQ kernels read,
+// in device memory that the code object itself holds, so that the entry
+// point allocates nothing. Every GPU the library runs on holds its own copy
+// until the process ends; every call on one GPU shares it.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                  int BH, int n_q, int n_k, int D, float scale, bool bf16,
+                                  hipStream_t stream) {
+  if (static_cast<int64_t>(BH) * n_q * static_cast<int64_t>(sizeof(float)) >
+      static_cast<int64_t>(kNoAllocScratchBytes))
+    return hipErrorInvalidValue;
+  // In host code `scratch` names a host-side stand-in, not the device array:
+  // its device address is looked up once per device, with that device
+  // current, and only that address is passed to the kernels.
+  static std::mutex mu;
+  static float* addr[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  float* delta = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+      void* p = nullptr;
+      err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (err != hipSuccess) return err;
+      addr[dev] = static_cast<float*>(p);
+    }
+    delta = addr[dev];
+  }
+  return launch_fa2_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, n_q, n_k, D, scale, bf16,
+                        stream);
+}
 
 hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,

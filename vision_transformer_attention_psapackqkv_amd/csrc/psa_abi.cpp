@@ -18,6 +18,9 @@
 #include "../../include/psa.h"
 #include "psa_launch.hpp"
 
+static_assert(psa::kNoAllocScratchBytes == PSA_NOALLOC_SCRATCH_BYTES,
+              "the scratch array and the limit the header states must agree");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -260,6 +263,44 @@ psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
   return launched(fn, [&] {
     return psa::launch_fa2_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, BH, n_q, n_k, head_dim,
                                scale, dtype == PSA_BF16, as_stream(stream));
+  });
+}
+
+psa_status fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int BH, int n_q, int n_k, int head_dim, float scale, psa_dtype dtype,
+                           void* stream) {
+  const char* fn = "fa2_bwd_noalloc";
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(PSA_ERR_NULL, fn, "every pointer argument is required");
+  PSA_TRY(check_attn(fn, BH, n_q, n_k, head_dim, scale, dtype));
+  const int64_t rows = static_cast<int64_t>(BH) * n_q;
+  if (rows > static_cast<int64_t>(PSA_NOALLOC_SCRATCH_BYTES / sizeof(float)))
+    return fail(PSA_ERR_SHAPE, fn,
+                "BH*n_q=%lld rows need %lld bytes of scratch; the limit is %lld bytes "
+                "(BH*n_q <= %lld): call fa2_bwd with a workspace instead",
+                static_cast<long long>(rows), static_cast<long long>(rows * 4),
+                static_cast<long long>(PSA_NOALLOC_SCRATCH_BYTES),
+                static_cast<long long>(PSA_NOALLOC_SCRATCH_BYTES / sizeof(float)));
+  const char* names[9] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
+  const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (int i = 0; i < 9; ++i) PSA_TRY(check_aligned(fn, names[i], ptrs[i]));
+  const int64_t eb = elt_bytes(dtype);
+  const int64_t nq = static_cast<int64_t>(BH) * n_q * head_dim;
+  const int64_t nk = static_cast<int64_t>(BH) * n_k * head_dim;
+  const Range outs[3] = {range("dq", dq, nq, eb), range("dk", dk, nk, eb), range("dv", dv, nk, eb)};
+  const Range ins[6] = {range("q", q, nq, eb),  range("k", k, nk, eb),
+                        range("v", v, nk, eb),  range("o", o, nq, eb),
+                        range("dout", dout, nq, eb), range("lse", lse, rows, 4)};
+  PSA_TRY(check_disjoint(fn, outs, 3));
+  for (const Range& a : outs)
+    for (const Range& b : ins) {
+      const Range pair[2] = {a, b};
+      PSA_TRY(check_disjoint(fn, pair, 2));
+    }
+  return launched(fn, [&] {
+    return psa::launch_fa2_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, BH, n_q, n_k, head_dim,
+                                       scale, dtype == PSA_BF16, as_stream(stream));
   });
 }
 

@@ -43,6 +43,14 @@ hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const voi
                           float* delta, int BH, int n_q, int n_k, int D, float scale, bool bf16,
                           hipStream_t stream);
 
+// fa2_bwd with -Delta in the library's own device scratch (no allocation, no
+// workspace argument): at most kNoAllocScratchBytes / 4 rows (BH * n_q).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                  int BH, int n_q, int n_k, int D, float scale, bool bf16,
+                                  hipStream_t stream);
+
 // Detect-decode: boxes [B, 4, A] LTRB (float32 or bf16) + anchor grid [A] x3 -> out [B, 4, A].
 hipError_t launch_detect_decode(const void* boxes, const float* anchor_x, const float* anchor_y,
                                 const float* strides, void* out, int B, int64_t A, bool bf16,
