@@ -492,7 +492,8 @@ def fa2_bwd_component(torch, psa, I, dev, steps, warm):
     wb = I.WORKLOADS["fa2_bwd_bf16_40x40"]
     q, k, v, do = (t.to(dev) for t in I.make_workload_bwd(wb))
     o, lse_b = psa.fa2_fwd(q, k, v)
-    ws = torch.empty((wb.BH * wb.N,), dtype=torch.float32, device=dev)
+    ws = torch.empty((psa.load_library().fa2_bwd_workspace_bytes(wb.BH, wb.N) // 4,), dtype=torch.float32,
+                     device=dev)
     avg, _, _ = time_events(lambda i: psa.fa2_bwd(q, k, v, o, do, lse_b, workspace=ws), steps, warm, torch)
     tb = 10.0 * wb.BH * wb.N ** 2 * wb.key_dim / (avg * 1e-3) / 1e12
     return {"avg_ms": round(avg, 5), "TFLOP/s": round(tb, 3), "pct_bf16_mfma_peak": round(100 * tb / PEAK_BF16_TFLOPS, 2),

@@ -142,8 +142,8 @@ psa_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
  * q, o, dout, dq: [BH, n_q, head_dim]; k, v, dk, dv: [BH, n_k, head_dim];
  * lse: [BH, n_q] float32 as written by fa2_fwd; workspace: caller-owned
  * float32 scratch of fa2_bwd_workspace_bytes(BH, n_q) bytes (the library keeps
- * -Delta there between its launches; its contents on return are not part of the
- * results).
+ * -Delta and LSE * log2(e) there between its launches; its contents on return
+ * are not part of the results).
  * scale must be the one given to fa2_fwd.
  */
 psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -151,18 +151,18 @@ psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
                    int BH, int n_q, int n_k, int head_dim, float scale, psa_dtype dtype,
                    void* stream);
 
-/* Bytes of workspace fa2_bwd needs: BH * n_q floats. 0 if a size is invalid. */
+/* Bytes of workspace fa2_bwd needs: 2 * BH * n_q floats. 0 if a size is invalid. */
 size_t fa2_bwd_workspace_bytes(int BH, int n_q);
 
 /*
  * fa2_bwd for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving or training loops, harnesses that forbid hipMalloc):
  * the same computation, results bit-identical to fa2_bwd's, with no workspace
- * argument. The -Delta rows live instead in a scratch array of
+ * argument. The -Delta and LSE * log2(e) rows live instead in a scratch array of
  * PSA_NOALLOC_SCRATCH_BYTES that the library's code object holds in device
  * memory; each GPU it runs on has its own copy, held until the process ends.
  * The entry point calls no allocating routine. Limit: BH * n_q <=
- * PSA_NOALLOC_SCRATCH_BYTES / 4 (4,194,304 rows); larger calls return
+ * PSA_NOALLOC_SCRATCH_BYTES / 8 (2,097,152 rows); larger calls return
  * PSA_ERR_SHAPE before anything is launched (use fa2_bwd with a workspace).
  * Every call on one GPU shares that scratch: calls whose executions overlap
  * on one GPU (on different streams, or from several host threads without

@@ -96,7 +96,7 @@ def test_fa2_fwd_argument_errors():
 
 def test_fa2_bwd_argument_errors():
     lib = psa.load_library()
-    assert lib.fa2_bwd_workspace_bytes(256, 1600) == 256 * 1600 * 4
+    assert lib.fa2_bwd_workspace_bytes(256, 1600) == 2 * 256 * 1600 * 4
     assert lib.fa2_bwd_workspace_bytes(0, 5) == 0
     base = [0x1000000 * (i + 1) for i in range(10)]
 
@@ -287,7 +287,7 @@ def test_fa2_bwd_noalloc_argument_errors():
     assert st == 3 and "head_dim=48" in msg
     st, msg = call(BH=0)
     assert st == 2 and msg.startswith("fa2_bwd_noalloc:")
-    limit = (16 << 20) // 4
+    limit = (16 << 20) // 8
     st, msg = call(BH=2, n_q=limit // 2 + 1, n_k=8)
     assert st == 2 and "scratch" in msg and str(16 << 20) in msg, msg
     st, msg = call(ptrs=p[:6] + [p[0]] + p[7:])

@@ -238,7 +238,7 @@ def fa2_bwd(q, k, v, o, dout, lse, scale=None, workspace=None):
     """FA2 backward; returns ``(dq, dk, dv)``.
 
     ``workspace``: a GPU tensor of at least ``fa2_bwd_workspace_bytes(BH, n_q)`` bytes
-    (BH * n_q floats), or None to allocate one."""
+    (2 * BH * n_q floats), or None to allocate one."""
     BH, n_q, D, n_k = _qkv3(q, k, v)
     _arg(o, "o", q.shape, q.dtype, like=q)
     _arg(dout, "dout", q.shape, q.dtype, like=q)
@@ -262,7 +262,7 @@ NOALLOC_SCRATCH_BYTES = 16 << 20   # PSA_NOALLOC_SCRATCH_BYTES of include/psa.h
 
 def fa2_bwd_noalloc(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None):
     """FA2 backward through ``fa2_bwd_noalloc``: no workspace, the library keeps -Delta in its
-    own device scratch (BH * n_q <= NOALLOC_SCRATCH_BYTES / 4). Returns ``(dq, dk, dv)``; pass
+    own device scratch (BH * n_q <= NOALLOC_SCRATCH_BYTES / 8). Returns ``(dq, dk, dv)``; pass
     them in to have nothing allocated at all. Calls that overlap on one GPU share that scratch
     and race; calls ordered on one stream do not."""
     BH, n_q, D, n_k = _qkv3(q, k, v)

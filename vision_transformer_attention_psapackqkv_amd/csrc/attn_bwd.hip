@@ -6,7 +6,7 @@
 // Delta = rowsum(dO * O) and dS = P * (dO V^T - Delta):
 //   dV = P^T dO,   dK = scale * dS^T Q,   dQ = scale * dS K.
 // Three launches: Delta (one pass over O and dO; stored negated, as the dP
-// accumulators start from -Delta), dK/dV (one workgroup per
+// accumulators start from -Delta, beside LSE * log2(e)), dK/dV (one workgroup per
 // key tile, looping over query tiles) and dQ (one workgroup per query tile,
 // looping over key tiles). Neither uses atomics.
 //
@@ -16,7 +16,9 @@
 // P and dS) are already the register operands of the next products, and the
 // LDS operands of those products, whose reduction index runs down the staged
 // rows, are read from the same row tiles with transposed LDS reads
-// (ds_read_b64_tr_b16). Tiles are staged once, as plain padded rows.
+// (ds_read_b64_tr_b16). Head dims 32..128 stage their tiles straight from
+// global memory into swizzled unpadded rows; head dim 16 through registers
+// into padded rows.
 #include <math.h>
 
 #include <mutex>
@@ -42,6 +44,7 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* delta;         // -Delta = -rowsum(dO o), [BH, n_q]
+  float* lse2;          // LSE * log2(e), [BH, n_q]
   int BH, n_q, n_k;
   int tiles;            // workgroups per batch-head
   float scale;
@@ -84,6 +87,7 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
     for (int d = 0; d < D; ++d) acc = fmaf(o[d], g[d], acc);
   }
   a.delta[row] = -acc;   // stored negated: the dP accumulators start from it
+  a.lse2[row] = a.lse[row] * kLog2e;
 }
 
 // ---------------------------------------------------------------- dK / dV (bf16)
@@ -460,6 +464,350 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
     }
 }
 
+// ---------------------------------------------------------------- direct staging (D >= 32)
+//
+// Head dims 32..128 with rows under 2 GB per batch-head stage their tiles
+// straight from global memory into LDS (buffer loads with an LDS destination):
+// no registers hold tile data and no LDS write or address instruction is
+// spent per tile. Tiles are 64 unpadded rows whose 16-byte chunks are placed
+// by packed_chunk_pos<D>, which keeps both read patterns of these kernels (the
+// 16-byte A-operand reads in key_of_row order and the transposed reads of rows
+// r and r + 4) free of bank conflicts. Rows past n lie outside the buffer
+// and read as zero: a zero Q/dO row (dK/dV kernel) or K/V row (dQ kernel)
+// contributes nothing to any product, so no tile is masked.
+
+// One 64-row tile of a [n][D] tensor: wave instruction b fills 1 KB block b
+// (512 / D rows), lane i the i-th chunk, fetching the global chunk the swizzle
+// puts there. The lane's offset is the same for every tile; the tile's first
+// row is a scalar offset. kUser tells the two kernels' instances apart: with
+// one instance shared by both kernels, this compiler left the host stub of the
+// second kernel launched undefined.
+template <int D, int kWaves, int kUser>
+struct RowStage {
+  static constexpr int CPR = D / 8;                    // chunks per row
+  static constexpr int RPB = 64 / CPR;                 // rows per 1 KB block
+  static constexpr int BLOCKS = 64 / RPB;
+  static constexpr int PER = (BLOCKS + kWaves - 1) / kWaves;
+  uint32_t voff[PER];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int row = (wave + i * kWaves) * RPB + lane / CPR;
+      voff[i] = static_cast<uint32_t>(row * D + packed_chunk_pos<D>(row, lane % CPR) * 8) * 2u;   // an involution
+    }
+  }
+
+  // `wave` must be wave-uniform.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, int row0, uint16_t* tile, int wave) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int b = wave + i * kWaves;
+      if (BLOCKS % kWaves != 0 && b >= BLOCKS) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(tile + b * 512),
+                                               16, voff[i], row0 * D * 2, 0, 0);
+    }
+  }
+};
+
+// 16 bytes of row `row`, chunk c, of a swizzled [64][D] tile.
+template <int D>
+__device__ __forceinline__ bf16x8 row_read8(const uint16_t* t, int row, int c) {
+  return *reinterpret_cast<const bf16x8*>(t + row * D + packed_chunk_pos<D>(row, c) * 8);
+}
+
+// One operand of 8 values down rows r .. r+7 at column col of a swizzled
+// [64][D] tile: transposed reads of rows r.. and r+4.. (see lds_read_tr8).
+template <int D>
+__device__ __forceinline__ bf16x8 row_read_tr8(const uint16_t* t, int r, int col) {
+  return lds_read_tr8_2(t + r * D + packed_chunk_pos<D>(r, col >> 3) * 8 + (col & 7),
+                        t + (r + 4) * D + packed_chunk_pos<D>(r + 4, col >> 3) * 8 + (col & 7));
+}
+
+template <int D, int kWaves>
+__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bwd_dkdv_direct(BwdArgs a) {
+  constexpr int BQ = 64;                 // queries per tile
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int T_EL = BQ * D;           // bf16 elements of one row tile
+  constexpr int BUF = 2 * T_EL + 4 * BQ; // Q and dO tiles, then LSE*log2(e) and -Delta (floats)
+  // Two tile buffers as two objects reached through restrict pointers, so the
+  // LDS reads of one tile need not wait for the direct loads into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t smem0[BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t smem1[BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, t16 = (lane >> 4) & 1;
+  int bh, kt;
+  block_of(a.BH * a.tiles, a.tiles, bh, kt);
+  const int key = kt * 32 * kWaves + wave * 32 + l32;
+  const bool k_ok = key < a.n_k;
+
+  // Tile sources: this batch-head's Q and dO rows and its LSE*log2(e) and
+  // -Delta values (each buffer ends at row n_q: rows past it read as zero).
+  const int64_t rows0 = static_cast<int64_t>(bh) * a.n_q;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.q + rows0 * D), 0, a.n_q * D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.dout + rows0 * D), 0, a.n_q * D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(a.lse2 + rows0, 0, a.n_q * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.delta + rows0, 0, a.n_q * 4, kBufferWord3);
+  RowStage<D, kWaves, 0> st;
+  st.init(wave, lane);
+  auto issue = [&](int qt, uint16_t* buf) {
+    st.issue(rq, qt * BQ, buf, wave);
+    st.issue(rg, qt * BQ, buf + T_EL, wave);
+    float* f = reinterpret_cast<float*>(buf + 2 * T_EL);
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)f, 4, lane * 4u,
+                                               qt * BQ * 4, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(f + BQ), 4,
+                                               lane * 4u, qt * BQ * 4, 0, 0);
+  };
+  const int n_tiles = (a.n_q + BQ - 1) / BQ;
+  issue(0, smem0);
+
+  // This lane's key and value rows as B operands: K[key][16ds + 8g + j]. Keys
+  // past n_k load row n_k - 1 (every load unconditional, all in flight
+  // together) and are zeroed afterwards.
+  bf16x8 kop[NDS], vop[NDS];
+  {
+    u32x4 kr[NDS], vr[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int64_t off = (static_cast<int64_t>(bh) * a.n_k + min(key, a.n_k - 1)) * D + ds * 16 + g * 8;
+      kr[ds] = load16(a.k + off);
+      vr[ds] = load16(a.v + off);
+    }
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      kop[ds] = as_bf16x8(k_ok ? kr[ds] : zero4());
+      vop[ds] = as_bf16x8(k_ok ? vr[ds] : zero4());
+    }
+  }
+  f32x16 dk_acc[NDB], dv_acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk_acc[db][r] = dv_acc[db][r] = 0.0f;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of tile 0 landed
+  __syncthreads();
+
+  // One query tile, read from h while the next one is loaded into nbuf.
+  auto tile = [&](int qt, const uint16_t* __restrict__ h, uint16_t* __restrict__ nbuf)
+                  __attribute__((always_inline)) {
+    const uint16_t* hg = h + T_EL;
+    const float* f = reinterpret_cast<const float*>(h + 2 * T_EL);
+    if (qt + 1 < n_tiles) issue(qt + 1, nbuf);
+
+    // The two 32-query blocks unrolled (every LDS address a per-lane offset
+    // plus a constant: the swizzle does not depend on the block) and kept one
+    // after the other by a scheduling barrier, so their registers do not overlap.
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      if (qb > 0) __builtin_amdgcn_sched_barrier(0);
+      // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries. Row rho of the
+      // A operands is query key_of_row(rho), so element r of lane group g holds
+      // query qb*32 + 16*(r/8) + 8g + r%8; dP's accumulator starts at -Delta.
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(f + BQ + qb * 32 + 16 * (r4 >> 1) + 8 * g + 4 * (r4 & 1));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sacc[4 * r4 + e] = 0.0f;
+          pacc[4 * r4 + e] = dl[e];
+        }
+      }
+      const int row = qb * 32 + key_of_row(l32);
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        sacc = mfma32x32x16(row_read8<D>(h, row, ds * 2 + g), kop[ds], sacc);
+        pacc = mfma32x32x16(row_read8<D>(hg, row, ds * 2 + g), vop[ds], pacc);
+      }
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(f + qb * 32 + 16 * (r4 >> 1) + 8 * g + 4 * (r4 & 1));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const float p = fast_exp2(fmaf(sacc[r], a.c, -l2[e]));
+          pb[r >> 3][r & 7] = static_cast<__bf16>(p);
+          sb[r >> 3][r & 7] = static_cast<__bf16>(p * pacc[r]);
+        }
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS over the block's queries, 16 per step.
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int r = (qb * 2 + s) * 16 + 8 * g + (i16 >> 2);
+          const int col = db * 32 + 16 * t16 + 4 * (i16 & 3);
+          dv_acc[db] = mfma32x32x16(row_read_tr8<D>(hg, r, col), pb[s], dv_acc[db]);
+          dk_acc[db] = mfma32x32x16(row_read_tr8<D>(h, r, col), sb[s], dk_acc[db]);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of the next tile landed
+    __syncthreads();
+  };
+  // Tile t lives in smem0 for even t, smem1 for odd. Two tiles per trip, so
+  // that each one reads a fixed LDS object: every LDS address is then a
+  // loop-invariant per-lane offset plus a constant.
+  int qt = 0;
+  for (; qt + 1 < n_tiles; qt += 2) {
+    tile(qt, smem0, smem1);
+    tile(qt + 1, smem1, smem0);
+  }
+  if (qt < n_tiles) tile(qt, smem0, smem1);
+
+  if (!k_ok) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + 8 * r4 + 4 * g;
+      const int64_t off = (static_cast<int64_t>(bh) * a.n_k + key) * D + d0;
+      uint32_t kw[2], vw[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        kw[e] = float_to_bf16_bits(dk_acc[db][4 * r4 + 2 * e] * a.scale) |
+                (uint32_t(float_to_bf16_bits(dk_acc[db][4 * r4 + 2 * e + 1] * a.scale)) << 16);
+        vw[e] = float_to_bf16_bits(dv_acc[db][4 * r4 + 2 * e]) |
+                (uint32_t(float_to_bf16_bits(dv_acc[db][4 * r4 + 2 * e + 1])) << 16);
+      }
+      *reinterpret_cast<u32x2*>(a.dk + off) = u32x2{kw[0], kw[1]};
+      *reinterpret_cast<u32x2*>(a.dv + off) = u32x2{vw[0], vw[1]};
+    }
+}
+
+template <int D, int kWaves>
+__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bwd_dq_direct(BwdArgs a) {
+  constexpr int BN = 64;                 // keys per tile
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int BM = 32 * kWaves;
+  constexpr int T_EL = BN * D;
+  __shared__ __attribute__((aligned(16))) uint16_t smem0[2 * T_EL];
+  __shared__ __attribute__((aligned(16))) uint16_t smem1[2 * T_EL];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, t16 = (lane >> 4) & 1;
+  int bh, qt;
+  block_of(a.BH * a.tiles, a.tiles, bh, qt);
+  const int q = qt * BM + wave * 32 + l32;
+  const bool q_ok = q < a.n_q;
+
+  const int64_t keys0 = static_cast<int64_t>(bh) * a.n_k;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.k + keys0 * D), 0, a.n_k * D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.v + keys0 * D), 0, a.n_k * D * 2, kBufferWord3);
+  RowStage<D, kWaves, 1> st;
+  st.init(wave, lane);
+  auto issue = [&](int kt, uint16_t* buf) {
+    st.issue(rk, kt * BN, buf, wave);
+    st.issue(rv, kt * BN, buf + T_EL, wave);
+  };
+  const int n_tiles = (a.n_k + BN - 1) / BN;
+  issue(0, smem0);
+
+  // This lane's query and dO rows as B operands. Queries past n_q load row
+  // n_q - 1 (all loads unconditional) and are zeroed afterwards; they are
+  // never stored.
+  bf16x8 qop[NDS], gop[NDS];
+  float l2, dl;
+  {
+    const int qc = min(q, a.n_q - 1);
+    u32x4 qr[NDS], gr[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int64_t off = (static_cast<int64_t>(bh) * a.n_q + qc) * D + ds * 16 + g * 8;
+      qr[ds] = load16(a.q + off);
+      gr[ds] = load16(a.dout + off);
+    }
+    const float lv = a.lse2[static_cast<int64_t>(bh) * a.n_q + qc];
+    const float dv = a.delta[static_cast<int64_t>(bh) * a.n_q + qc];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      qop[ds] = as_bf16x8(q_ok ? qr[ds] : zero4());
+      gop[ds] = as_bf16x8(q_ok ? gr[ds] : zero4());
+    }
+    l2 = q_ok ? lv : 0.0f;
+    dl = q_ok ? dv : 0.0f;
+  }
+  f32x16 dq_acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.0f;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of tile 0 landed
+  __syncthreads();
+
+  auto tile = [&](int kt, const uint16_t* __restrict__ ks, uint16_t* __restrict__ nbuf)
+                  __attribute__((always_inline)) {
+    const uint16_t* vs = ks + T_EL;
+    if (kt + 1 < n_tiles) issue(kt + 1, nbuf);
+    bf16x8 sb[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T (from -Delta). Row rho of
+      // the A operands is key key_of_row(rho): element r of lane group g holds
+      // key 16*(r/8) + 8g + r%8 of the block, so dS comes out as the B operand
+      // of the dQ product.
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[r] = 0.0f;
+        pacc[r] = dl;
+      }
+      const int row = kb * 32 + key_of_row(l32);
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        sacc = mfma32x32x16(row_read8<D>(ks, row, ds * 2 + g), qop[ds], sacc);
+        pacc = mfma32x32x16(row_read8<D>(vs, row, ds * 2 + g), gop[ds], pacc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sacc[r], a.c, -l2));
+        sb[kb * 2 + (r >> 3)][r & 7] = static_cast<__bf16>(p * pacc[r]);
+      }
+    }
+    // dQ^T += K^T dS^T over the tile's keys; K^T through transposed reads.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int s = 0; s < BN / 16; ++s)
+        dq_acc[db] = mfma32x32x16(row_read_tr8<D>(ks, s * 16 + 8 * g + (i16 >> 2), db * 32 + 16 * t16 + 4 * (i16 & 3)),
+                                  sb[s], dq_acc[db]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of the next tile landed
+    __syncthreads();
+  };
+  int kt = 0;   // two tiles per trip, as in the dK/dV kernel
+  for (; kt + 1 < n_tiles; kt += 2) {
+    tile(kt, smem0, smem1);
+    tile(kt + 1, smem1, smem0);
+  }
+  if (kt < n_tiles) tile(kt, smem0, smem1);
+
+  if (!q_ok) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + 8 * r4 + 4 * g;
+      uint32_t w[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        w[e] = float_to_bf16_bits(dq_acc[db][4 * r4 + 2 * e] * a.scale) |
+               (uint32_t(float_to_bf16_bits(dq_acc[db][4 * r4 + 2 * e + 1] * a.scale)) << 16);
+      *reinterpret_cast<u32x2*>(a.dq + (static_cast<int64_t>(bh) * a.n_q + q) * D + d0) = u32x2{w[0], w[1]};
+    }
+}
+
 // ---------------------------------------------------------------- float32
 
 constexpr int kF32Threads = 128;
@@ -579,6 +927,28 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dq_f32(BwdArgs a) {
 
 constexpr int kWavesBwd = 4;
 
+// Direct staging needs head dim 32..128 and every batch-head's rows under
+// 2 GB (32-bit buffer offsets).
+bool bwd_direct(int D, int n_q, int n_k) {
+  const int64_t n = n_q > n_k ? n_q : n_k;
+  return D >= 32 && n * D * 2 < (int64_t(1) << 31);
+}
+
+// The direct-staged dK/dV and dQ launches (head dims 32..128; false for 16).
+template <int D>
+typename std::enable_if<(D >= 32), bool>::type launch_direct(const BwdArgs& kv, dim3 grid_kv, const BwdArgs& qa,
+                                                              dim3 grid_q, hipStream_t stream) {
+  if (!bwd_direct(D, kv.n_q, kv.n_k)) return false;
+  bwd_dkdv_direct<D, kWavesBwd><<<grid_kv, kWavesBwd * 64, 0, stream>>>(kv);
+  bwd_dq_direct<D, kWavesBwd><<<grid_q, kWavesBwd * 64, 0, stream>>>(qa);
+  return true;
+}
+template <int D>
+typename std::enable_if<(D < 32), bool>::type launch_direct(const BwdArgs&, dim3, const BwdArgs&, dim3,
+                                                             hipStream_t) {
+  return false;
+}
+
 template <int D>
 hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.BH) * a.n_q;
@@ -587,10 +957,13 @@ hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
     bwd_delta<D, true><<<grid_delta, 256, 0, stream>>>(a);
     BwdArgs kv = a;
     kv.tiles = (a.n_k + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
-    bwd_dkdv_bf16<D, kWavesBwd><<<dim3(static_cast<unsigned>(a.BH) * kv.tiles), kWavesBwd * 64, 0, stream>>>(kv);
+    const dim3 grid_kv(static_cast<unsigned>(a.BH) * kv.tiles);
     BwdArgs qa = a;
     qa.tiles = (a.n_q + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
-    bwd_dq_bf16<D, kWavesBwd><<<dim3(static_cast<unsigned>(a.BH) * qa.tiles), kWavesBwd * 64, 0, stream>>>(qa);
+    const dim3 grid_q(static_cast<unsigned>(a.BH) * qa.tiles);
+    if (launch_direct<D>(kv, grid_kv, qa, grid_q, stream)) return hipGetLastError();
+    bwd_dkdv_bf16<D, kWavesBwd><<<grid_kv, kWavesBwd * 64, 0, stream>>>(kv);
+    bwd_dq_bf16<D, kWavesBwd><<<grid_q, kWavesBwd * 64, 0, stream>>>(qa);
   } else {
     bwd_delta<D, false><<<grid_delta, 256, 0, stream>>>(a);
     const unsigned kb = (a.n_k + kF32Threads - 1) / kF32Threads;
@@ -603,7 +976,7 @@ hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
 
 }  // namespace
 
-// Scratch of fa2_bwd_noalloc: the -Delta rows the dK/dV and dQ kernels read,
+// Scratch of fa2_bwd_noalloc: the -Delta and LSE*log2(e) rows the dK/dV and dQ kernels read,
 // in device memory that the code object itself holds, so that the entry
 // point allocates nothing. Every GPU the library runs on holds its own copy
 // until the process ends; every call on one GPU shares it.
@@ -613,7 +986,7 @@ hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, c
                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
                                   int BH, int n_q, int n_k, int D, float scale, bool bf16,
                                   hipStream_t stream) {
-  if (static_cast<int64_t>(BH) * n_q * static_cast<int64_t>(sizeof(float)) >
+  if (static_cast<int64_t>(BH) * n_q * static_cast<int64_t>(2 * sizeof(float)) >
       static_cast<int64_t>(kNoAllocScratchBytes))
     return hipErrorInvalidValue;
   // In host code `scratch` names a host-side stand-in, not the device array:
@@ -625,7 +998,7 @@ hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, c
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  float* delta = nullptr;
+  float* ws = nullptr;
   {
     std::lock_guard<std::mutex> lock(mu);
     if (addr[dev] == nullptr) {
@@ -634,20 +1007,22 @@ hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, c
       if (err != hipSuccess) return err;
       addr[dev] = static_cast<float*>(p);
     }
-    delta = addr[dev];
+    ws = addr[dev];
   }
-  return launch_fa2_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, n_q, n_k, D, scale, bf16,
+  return launch_fa2_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, BH, n_q, n_k, D, scale, bf16,
                         stream);
 }
 
 hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                          float* delta, int BH, int n_q, int n_k, int D, float scale, bool bf16,
+                          float* workspace, int BH, int n_q, int n_k, int D, float scale, bool bf16,
                           hipStream_t stream) {
+  float* delta = workspace;
+  float* lse2 = workspace + static_cast<int64_t>(BH) * n_q;
   BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
             static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
             static_cast<const uint16_t*>(dout), lse, static_cast<uint16_t*>(dq),
-            static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), delta, BH, n_q, n_k, 0,
+            static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), delta, lse2, BH, n_q, n_k, 0,
             scale, scale * kLog2e};
   switch (D) {
     case 16: return run<16>(a, bf16, stream);

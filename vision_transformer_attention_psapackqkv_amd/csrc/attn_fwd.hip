@@ -218,21 +218,6 @@ struct FwdStageDirect {
   }
 };
 
-// Position of 16-byte chunk c of row `row` in an unpadded packed tile of D
-// columns (D/8 chunks per row): an XOR swizzle chosen so that neither the
-// K-operand reads (16 bytes per lane, rows in key_of_row order) nor the
-// transposed V-operand reads (8 bytes per lane, rows r and r + 4) of one
-// instruction meet twice on a bank.
-template <int D>
-__device__ __forceinline__ int packed_chunk_pos(int row, int c) {
-  static_assert(D == 32 || D == 64 || D == 128, "packed direct staging");
-  if constexpr (D == 32) return c ^ ((row >> 2) & 3);
-  if constexpr (D == 64)
-    return c ^ (((row >> 1) & 1) | (((row >> 2) & 1) << 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 2));
-  return c ^ ((row & 1) | (((row >> 1) & 1) << 1) | (((row ^ (row >> 2)) & 1) << 2) |
-              ((((row >> 1) ^ (row >> 3)) & 1) << 3));
-}
-
 // Direct global -> LDS staging of one packed key tile ([BH, n, D] K and V,
 // D >= 32): 64 rows of D elements each, unpadded, chunks placed by
 // packed_chunk_pos. Wave instruction b fills one 1 KB block (512 / D rows);

@@ -503,15 +503,21 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
     if (more) finish(nbuf);
     __syncthreads();
   };
-  // Tile t lives in smem0 for even t, smem1 for odd.
-  for (int kt = 0; kt + 1 < n_tiles; ++kt) {
-    const bool odd = kt & 1;
-    tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1, std::false_type{});
+  // Tile t lives in smem0 for even t, smem1 for odd. Two tiles per trip, so
+  // that each reads a fixed LDS object and every LDS address is a
+  // loop-invariant per-lane offset plus a constant (-1.1 % on the 40x40 map;
+  // the dK/dV kernel, where the same change costs registers it lacks, keeps
+  // one tile per trip). The last tile masks keys past N.
+  int kt = 0;
+  for (; kt + 2 < n_tiles; kt += 2) {
+    tile(kt, smem0, smem1, std::false_type{});
+    tile(kt + 1, smem1, smem0, std::false_type{});
   }
-  {
-    const int kt = n_tiles - 1;
-    const bool odd = kt & 1;
-    tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1, std::true_type{});
+  if (kt + 1 < n_tiles) {
+    tile(kt, smem0, smem1, std::false_type{});
+    tile(kt + 1, smem1, smem0, std::true_type{});
+  } else {
+    tile(kt, smem0, smem1, std::true_type{});
   }
 
   if (!q_ok) return;

@@ -232,7 +232,7 @@ psa_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t fa2_bwd_workspace_bytes(int BH, int n_q) {
   if (BH <= 0 || n_q <= 0) return 0;
-  return static_cast<size_t>(BH) * static_cast<size_t>(n_q) * sizeof(float);
+  return 2 * static_cast<size_t>(BH) * static_cast<size_t>(n_q) * sizeof(float);
 }
 
 psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -250,7 +250,7 @@ psa_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
   const int64_t nk = static_cast<int64_t>(BH) * n_k * head_dim;
   const int64_t rows = static_cast<int64_t>(BH) * n_q;
   const Range outs[4] = {range("dq", dq, nq, eb), range("dk", dk, nk, eb), range("dv", dv, nk, eb),
-                         range("workspace", workspace, rows, 4)};
+                         range("workspace", workspace, 2 * rows, 4)};
   const Range ins[6] = {range("q", q, nq, eb),  range("k", k, nk, eb),
                         range("v", v, nk, eb),  range("o", o, nq, eb),
                         range("dout", dout, nq, eb), range("lse", lse, rows, 4)};
@@ -275,13 +275,13 @@ psa_status fa2_bwd_noalloc(const void* q, const void* k, const void* v, const vo
     return fail(PSA_ERR_NULL, fn, "every pointer argument is required");
   PSA_TRY(check_attn(fn, BH, n_q, n_k, head_dim, scale, dtype));
   const int64_t rows = static_cast<int64_t>(BH) * n_q;
-  if (rows > static_cast<int64_t>(PSA_NOALLOC_SCRATCH_BYTES / sizeof(float)))
+  if (rows > static_cast<int64_t>(PSA_NOALLOC_SCRATCH_BYTES / (2 * sizeof(float))))
     return fail(PSA_ERR_SHAPE, fn,
                 "BH*n_q=%lld rows need %lld bytes of scratch; the limit is %lld bytes "
                 "(BH*n_q <= %lld): call fa2_bwd with a workspace instead",
-                static_cast<long long>(rows), static_cast<long long>(rows * 4),
+                static_cast<long long>(rows), static_cast<long long>(rows * 8),
                 static_cast<long long>(PSA_NOALLOC_SCRATCH_BYTES),
-                static_cast<long long>(PSA_NOALLOC_SCRATCH_BYTES / sizeof(float)));
+                static_cast<long long>(PSA_NOALLOC_SCRATCH_BYTES / (2 * sizeof(float))));
   const char* names[9] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"};
   const void* ptrs[9] = {q, k, v, o, dout, lse, dq, dk, dv};
   for (int i = 0; i < 9; ++i) PSA_TRY(check_aligned(fn, names[i], ptrs[i]));

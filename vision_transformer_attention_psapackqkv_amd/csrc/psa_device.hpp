@@ -95,6 +95,21 @@ __device__ __forceinline__ int tr_key_col(int s) { return ((s & 1) << 3) | ((s &
 // instruction reads together on 16 different bank groups.
 __device__ __forceinline__ int tile_chunk_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
 
+// Position of 16-byte chunk c of row `row` in an unpadded tile of packed rows
+// of D columns (D/8 chunks per row): an XOR swizzle chosen so that neither the
+// 16-byte operand reads (rows in key_of_row order) nor the transposed 8-byte
+// operand reads (rows r and r + 4) of one instruction meet twice on a bank.
+// Both attention directions read their packed row tiles in these two ways.
+template <int D>
+__device__ __forceinline__ int packed_chunk_pos(int row, int c) {
+  static_assert(D == 32 || D == 64 || D == 128, "packed direct staging");
+  if constexpr (D == 32) return c ^ ((row >> 2) & 3);
+  if constexpr (D == 64)
+    return c ^ (((row >> 1) & 1) | (((row >> 2) & 1) << 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 2));
+  return c ^ ((row & 1) | (((row >> 1) & 1) << 1) | (((row ^ (row >> 2)) & 1) << 2) |
+              ((((row >> 1) ^ (row >> 3)) & 1) << 3));
+}
+
 // Word 3 of a gfx9 buffer resource for raw (untyped, unswizzled) byte-offset
 // loads: data format 32 so the hardware does not treat the buffer as invalid.
 constexpr int kBufferWord3 = 0x00020000;

@@ -37,14 +37,15 @@ hipError_t launch_psa_fused_bwd(const void* qkv, const void* out, const float* l
                                 const void* dvres, void* dqkv, float* workspace, int BH, int KD,
                                 int N, float scale, hipStream_t stream);
 
-// FA2 backward: -Delta into the workspace, then the dK/dV and dQ kernels.
+// FA2 backward: -Delta and LSE * log2(e) into the workspace (2 * BH * n_q
+// floats), then the dK/dV and dQ kernels.
 hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                          float* delta, int BH, int n_q, int n_k, int D, float scale, bool bf16,
+                          float* workspace, int BH, int n_q, int n_k, int D, float scale, bool bf16,
                           hipStream_t stream);
 
 // fa2_bwd with -Delta in the library's own device scratch (no allocation, no
-// workspace argument): at most kNoAllocScratchBytes / 4 rows (BH * n_q).
+// workspace argument): at most kNoAllocScratchBytes / 8 rows (BH * n_q).
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
