@@ -335,6 +335,139 @@ struct FwdStage {
   }
 };
 
+// ---- pieces of the forward kernel (NCHW and packed)
+
+// V residual workgroups (NCHW, N a multiple of 8): queued after every
+// attention workgroup, they run on the slots the grid's last partial round
+// leaves free. A batch-head's V channels are DV*N contiguous elements on both
+// sides, so the residual is a plain copy of BH such blocks. Workgroup w
+// (counted from the first residual workgroup) copies every vres_wgs-th chunk.
+template <int KD, int DV, int NT>
+__device__ __forceinline__ void vres_copy_wg(const FwdArgs& a, int N, int w, int tid) {
+  const int64_t per_bh = static_cast<int64_t>(DV) * N / 8;   // 16-byte chunks
+  const int64_t total = per_bh * a.BH;
+  const int64_t stride = static_cast<int64_t>(a.vres_wgs) * NT;
+  constexpr int BATCH = 8;
+  for (int64_t c0 = static_cast<int64_t>(w) * NT + tid; c0 < total; c0 += stride * BATCH) {
+    u32x4 r[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int64_t c = min(c0 + u * stride, total - 1);
+      const int64_t bh_c = c / per_bh;
+      r[u] = ldg_nt(reinterpret_cast<const u32x4*>(a.v + (bh_c * 4 * KD + 2 * KD) * N + (c - bh_c * per_bh) * 8));
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int64_t c = c0 + u * stride;
+      const int64_t bh_c = c / per_bh;
+      if (c < total) stg_nt(reinterpret_cast<u32x4*>(a.vres + bh_c * DV * N + (c - bh_c * per_bh) * 8), r[u]);
+    }
+  }
+}
+
+// Work unit of attention workgroup i: a whole query tile (split = -1), or key
+// tiles [kt0, kt1) (piece `piece`) of split tile `split`. L is the logical
+// query tile.
+__device__ __forceinline__ void work_unit(const FwdArgs& a, int i, int n_tiles, int& L, int& split, int& piece,
+                                          int& kt0, int& kt1) {
+  split = -1;
+  piece = 0;
+  kt0 = 0;
+  kt1 = n_tiles;
+  if (i < a.full) {
+    L = full_tile(a, i);
+    return;
+  }
+  const int j = i - a.full;   // pieces of one split tile stay on one XCD
+  if (xcd_order(a)) {
+    const int local = j / 8;
+    split = (local / a.splits) * 8 + j % 8;
+    piece = local % a.splits;
+  } else {
+    split = j / a.splits;
+    piece = j % a.splits;
+  }
+  L = split_tile(a, split);
+  kt0 = piece * n_tiles / a.splits;
+  kt1 = (piece + 1) * n_tiles / a.splits;
+}
+
+// V residual of one query tile (NCHW, N a multiple of 8): this tile's pixel
+// columns of the V channels. The loads of a batch are unconditional (chunks
+// past the map's last pixel re-read its last chunk; only the stores are
+// guarded), so they are all in flight together.
+template <int KD, int DV, int NT, int BM>
+__device__ __forceinline__ void vres_copy_tile(const FwdArgs& a, int bh, int qt, int N, int tid) {
+  const int n0 = qt * BM;
+  constexpr int CPR = BM / 8;   // 8-pixel chunks per channel row
+  constexpr int TOTAL = DV * CPR;
+  static_assert(TOTAL % NT == 0, "V residual chunks per thread");
+  constexpr int PER = TOTAL / NT;
+  constexpr int BATCH = PER < 8 ? PER : 8;
+#pragma unroll
+  for (int u0 = 0; u0 < PER; u0 += BATCH) {
+    u32x4 r[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int c = (u0 + u) * NT + tid, dv = c / CPR, n = n0 + (c % CPR) * 8;
+      r[u] = load16(a.v + (static_cast<int64_t>(bh) * 4 * KD + 2 * KD + dv) * N + min(n, N - 8));
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int c = (u0 + u) * NT + tid, dv = c / CPR, n = n0 + (c % CPR) * 8;
+      if (n < N) stg_nt(reinterpret_cast<u32x4*>(a.vres + (static_cast<int64_t>(bh) * DV + dv) * N + n), r[u]);
+    }
+  }
+}
+
+// End of a work unit. A whole query tile: O = O^T / l in bf16, LSE =
+// (m + log2 l) ln 2. A piece of a split tile: its unnormalised O^T, running
+// max and sum, for the merge kernel. ql = this lane's query within the tile.
+template <int DV, int NDB, int BM, int PART, bool kNCHW>
+__device__ __forceinline__ void store_result(const FwdArgs& a, const f32x16 (&oacc)[NDB], float m_run, float l_tot,
+                                             int bh, int q_row, bool q_ok, int split, int piece, int ql, int g) {
+  const int N = a.n_k;
+  if (split < 0) {
+    const float inv = 1.0f / l_tot;
+    if (!q_ok) return;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dv0 = db * 32 + 8 * r4 + 4 * g;
+        if (dv0 >= DV) continue;
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(oacc[db][4 * r4 + e] * inv);
+        if constexpr (kNCHW) {
+          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * DV + dv0) * N + q_row;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[static_cast<int64_t>(e) * N] = h[e];
+        } else {
+          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * a.n_q + q_row) * DV + dv0;
+          *reinterpret_cast<u32x2*>(dst) = u32x2{h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16)};
+        }
+      }
+    if (a.lse != nullptr && g == 0)
+      a.lse[static_cast<int64_t>(bh) * a.n_q + q_row] = (m_run + log2f(l_tot)) * kLn2;
+    return;
+  }
+  float* pp = a.part + (static_cast<int64_t>(split) * a.splits + piece) * PART;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dv0 = db * 32 + 8 * r4 + 4 * g;
+      if (dv0 >= DV) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pp[(dv0 + e) * BM + ql] = oacc[db][4 * r4 + e];
+    }
+  if (g == 0) {
+    pp[DV * BM + ql] = m_run;
+    pp[DV * BM + BM + ql] = l_tot;
+  }
+}
+
 // kOcc: waves per SIMD the register allocation must allow.
 template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
 __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
@@ -369,49 +502,13 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   if constexpr (kNCHW && kVecN) {
     const int n_attn = a.full + a.tail * a.splits;
     if (a.vres_wgs > 0 && static_cast<int>(blockIdx.x) >= n_attn) {
-      const int64_t per_bh = static_cast<int64_t>(DV) * N / 8;   // 16-byte chunks
-      const int64_t total = per_bh * a.BH;
-      const int64_t stride = static_cast<int64_t>(a.vres_wgs) * NT;
-      constexpr int BATCH = 8;
-      for (int64_t c0 = static_cast<int64_t>(blockIdx.x - n_attn) * NT + tid; c0 < total; c0 += stride * BATCH) {
-        u32x4 r[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const int64_t c = min(c0 + u * stride, total - 1);
-          const int64_t bh_c = c / per_bh;
-          r[u] = ldg_nt(reinterpret_cast<const u32x4*>(a.v + (bh_c * 4 * KD + 2 * KD) * N + (c - bh_c * per_bh) * 8));
-        }
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const int64_t c = c0 + u * stride;
-          const int64_t bh_c = c / per_bh;
-          if (c < total) stg_nt(reinterpret_cast<u32x4*>(a.vres + bh_c * DV * N + (c - bh_c * per_bh) * 8), r[u]);
-        }
-      }
+      vres_copy_wg<KD, DV, NT>(a, N, static_cast<int>(blockIdx.x) - n_attn, tid);
       return;
     }
   }
 
-  // Work unit: a whole query tile, or key tiles [kt0, kt1) (piece `piece`) of
-  // split tile `split`.
-  int L, split = -1, piece = 0, kt0 = 0, kt1 = n_tiles;
-  const int i = blockIdx.x;
-  if (i < a.full) {
-    L = full_tile(a, i);
-  } else {
-    const int j = i - a.full;   // pieces of one split tile stay on one XCD
-    if (xcd_order(a)) {
-      const int local = j / 8;
-      split = (local / a.splits) * 8 + j % 8;
-      piece = local % a.splits;
-    } else {
-      split = j / a.splits;
-      piece = j % a.splits;
-    }
-    L = split_tile(a, split);
-    kt0 = piece * n_tiles / a.splits;
-    kt1 = (piece + 1) * n_tiles / a.splits;
-  }
+  int L, split, piece, kt0, kt1;
+  work_unit(a, blockIdx.x, n_tiles, L, split, piece, kt0, kt1);
   const int bh = L / a.q_tiles;
   const int qt = L - bh * a.q_tiles;
   const int q_row = qt * BM + wave * 32 + l32;
@@ -438,33 +535,15 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   }
 
   // V residual: copy this tile's pixel columns of the V channels (NCHW only;
-  // the first piece of a split tile does it). With 16-byte rows the loads of a
-  // batch are unconditional (chunks past the map's last pixel re-read its last
-  // chunk; only the stores are guarded), so they are all in flight together.
+  // the first piece of a split tile does it).
   if constexpr (kNCHW) {
     if (a.vres != nullptr && piece == 0 && a.vres_wgs == 0) {
-      const int n0 = qt * BM;
-      constexpr int CPR = BM / 8;   // 8-pixel chunks per channel row
-      constexpr int TOTAL = DV * CPR;
       if constexpr (kVecN) {
-        static_assert(TOTAL % NT == 0, "V residual chunks per thread");
-        constexpr int PER = TOTAL / NT;
-        constexpr int BATCH = PER < 8 ? PER : 8;
-#pragma unroll
-        for (int u0 = 0; u0 < PER; u0 += BATCH) {
-          u32x4 r[BATCH];
-#pragma unroll
-          for (int u = 0; u < BATCH; ++u) {
-            const int c = (u0 + u) * NT + tid, dv = c / CPR, n = n0 + (c % CPR) * 8;
-            r[u] = load16(a.v + (static_cast<int64_t>(bh) * 4 * KD + 2 * KD + dv) * N + min(n, N - 8));
-          }
-#pragma unroll
-          for (int u = 0; u < BATCH; ++u) {
-            const int c = (u0 + u) * NT + tid, dv = c / CPR, n = n0 + (c % CPR) * 8;
-            if (n < N) stg_nt(reinterpret_cast<u32x4*>(a.vres + (static_cast<int64_t>(bh) * DV + dv) * N + n), r[u]);
-          }
-        }
+        vres_copy_tile<KD, DV, NT, BM>(a, bh, qt, N, tid);
       } else {
+        const int n0 = qt * BM;
+        constexpr int CPR = BM / 8;   // 8-pixel chunks per channel row
+        constexpr int TOTAL = DV * CPR;
         for (int c = tid; c < TOTAL; c += NT) {
           const int dv = c / CPR, n = n0 + (c % CPR) * 8;
           const uint16_t* src = a.v + (static_cast<int64_t>(bh) * 4 * KD + 2 * KD + dv) * N + n;
@@ -628,53 +707,7 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   }
 
   const float l_tot = l_run + lane_xor32(l_run, g);
-
-  if (split < 0) {
-    // Whole tile: O = O^T / l, LSE = (m + log2 l) ln 2.
-    const float inv = 1.0f / l_tot;
-    if (!q_ok) return;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dv0 = db * 32 + 8 * r4 + 4 * g;
-        if (dv0 >= DV) continue;
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(oacc[db][4 * r4 + e] * inv);
-        if constexpr (kNCHW) {
-          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * DV + dv0) * N + q_row;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[static_cast<int64_t>(e) * N] = h[e];
-        } else {
-          uint16_t* dst = a.o + (static_cast<int64_t>(bh) * a.n_q + q_row) * DV + dv0;
-          *reinterpret_cast<u32x2*>(dst) = u32x2{h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16)};
-        }
-      }
-    if (a.lse != nullptr && g == 0)
-      a.lse[static_cast<int64_t>(bh) * a.n_q + q_row] = (m_run + log2f(l_tot)) * kLn2;
-    return;
-  }
-
-  // Piece of a split tile: store unnormalised O^T, the running max and sum
-  // for the merge kernel.
-  {
-    float* pp = a.part + (static_cast<int64_t>(split) * a.splits + piece) * C::PART;
-    const int ql = wave * 32 + l32;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dv0 = db * 32 + 8 * r4 + 4 * g;
-        if (dv0 >= DV) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pp[(dv0 + e) * BM + ql] = oacc[db][4 * r4 + e];
-      }
-    if (g == 0) {
-      pp[DV * BM + ql] = m_run;
-      pp[DV * BM + BM + ql] = l_tot;
-    }
-  }
+  store_result<DV, NDB, BM, C::PART, kNCHW>(a, oacc, m_run, l_tot, bh, q_row, q_ok, split, piece, wave * 32 + l32, g);
 }
 
 // Merge of split tiles. One workgroup per (split tile, 8 rows of O^T); each
@@ -865,37 +898,46 @@ struct FwdPlan {
   size_t bytes;
 };
 
-template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
-FwdPlan plan_bf16(int BH, int n_q, int n_k) {
-  using C = FwdCfg<KD, DV, kNCHW, kWaves, direct_staging<KD, kNCHW, kVecN>()>;
-  // Resident workgroups per CU (the same on every gfx950), cached atomically:
-  // threads that fill the cache at the same time all store the same value.
-  static std::atomic<int> occ_cache{-1};
-  int occ = occ_cache.load(std::memory_order_relaxed);
-  if (occ < 0) {
-    int n = 0;
-    occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &n, reinterpret_cast<const void*>(attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>),
-              C::NT, 0) == hipSuccess ? n : 0;
-    occ_cache.store(occ, std::memory_order_relaxed);
-  }
+// Query tiles and split plan for `occ` resident workgroups per CU of BM queries each.
+FwdPlan make_plan(int occ, int BM, int part_floats, int BH, int n_q, int n_k) {
   FwdPlan p;
-  p.q_tiles = (n_q + C::BM - 1) / C::BM;
+  p.q_tiles = (n_q + BM - 1) / BM;
   const int total = BH * p.q_tiles;
   int rem = 0;
   p.slots = occ * cu_count();
   p.splits = tail_splits(total, p.slots, (n_k + kBN - 1) / kBN, rem);
   p.tail = rem;
   p.full = total - rem;
-  p.bytes = sizeof(float) * static_cast<size_t>(C::PART) * rem * p.splits;
+  p.bytes = sizeof(float) * static_cast<size_t>(part_floats) * rem * p.splits;
   return p;
 }
 
-// Launches the forward; splits the tail only if `ws` holds the plan's bytes.
+// Resident workgroups per CU of a kernel (the same on every gfx950), cached
+// atomically per kernel: threads that fill a cache at the same time all store
+// the same value.
+template <typename K>
+int occupancy(K kernel, int threads, std::atomic<int>& cache) {
+  int occ = cache.load(std::memory_order_relaxed);
+  if (occ < 0) {
+    int n = 0;
+    occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), threads, 0) ==
+                  hipSuccess ? n : 0;
+    cache.store(occ, std::memory_order_relaxed);
+  }
+  return occ;
+}
+
 template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
-hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
+FwdPlan plan_bf16(int BH, int n_q, int n_k) {
   using C = FwdCfg<KD, DV, kNCHW, kWaves, direct_staging<KD, kNCHW, kVecN>()>;
-  FwdPlan p = plan_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>(a.BH, a.n_q, a.n_k);
+  static std::atomic<int> occ_cache{-1};
+  const int occ = occupancy(attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>, C::NT, occ_cache);
+  return make_plan(occ, C::BM, C::PART, BH, n_q, n_k);
+}
+
+// Sets the launch fields of `a` from plan p (splitting the tail only if `ws`
+// holds the plan's bytes) and returns the number of attention workgroups.
+int apply_plan(FwdArgs& a, FwdPlan& p, void* ws, size_t ws_bytes, bool vres_wgs_ok) {
   if (p.tail > 0 && (ws == nullptr || ws_bytes < p.bytes)) {
     p.full += p.tail;
     p.tail = 0;
@@ -913,10 +955,19 @@ hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream)
   // round of whole query tiles measured slower).
   const int n_attn = p.full + p.tail * p.splits;
   a.vres_wgs = 0;
-  if (kNCHW && kVecN && a.vres != nullptr && p.tail > 0 && p.slots > 0) {
+  if (vres_wgs_ok && a.vres != nullptr && p.tail > 0 && p.slots > 0) {
     const int last = n_attn % p.slots;
     if (last != 0 && p.slots - last >= kMinVresWgs) a.vres_wgs = p.slots - last;
   }
+  return n_attn;
+}
+
+// Launches the forward; splits the tail only if `ws` holds the plan's bytes.
+template <int KD, int DV, bool kNCHW, bool kVecN, int kWaves, int kOcc>
+hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  using C = FwdCfg<KD, DV, kNCHW, kWaves, direct_staging<KD, kNCHW, kVecN>()>;
+  FwdPlan p = plan_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>(a.BH, a.n_q, a.n_k);
+  const int n_attn = apply_plan(a, p, ws, ws_bytes, kNCHW && kVecN);
   attn_fwd_bf16<KD, DV, kNCHW, kVecN, kWaves, kOcc>
       <<<dim3(static_cast<unsigned>(n_attn + a.vres_wgs)), C::NT, 0, stream>>>(a);
   if (p.tail > 0) {
@@ -928,7 +979,6 @@ hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream)
   }
   return hipGetLastError();
 }
-
 
 // Workgroups per CU the registers must allow for head dims up to 64: three
 // where the LDS also holds three (directly staged NCHW tiles, key_dim 64),
