@@ -635,16 +635,19 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     }
 
     // Online softmax: running max, rescale, P = 2^(c*S - m).
-    float mx = sacc[0][0];
+    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, lane_xor32(mx, g));
     // The running max only moves when some lane's tile max exceeds it by more
     // than 8 (log2 units): until then P <= 2^8, harmless in fp32 and bf16. The
     // test is on the raw scores, against the threshold kept since the last move.
+    // A query's keys are split between lanes l and l ^ 32, which hold the same
+    // threshold, so testing each lane's own half decides exactly as testing the
+    // whole row would; the row max itself is only needed when the max moves.
     if (__any(mx > m_thr)) {
+      mx = fmaxf(mx, lane_xor32(mx, g));
       const float m_new = fmaxf(m_run, mx * a.c);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
@@ -700,10 +703,21 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     __syncthreads();
   };
 
-  // Tile kt0 + 2i lives in smem0, kt0 + 2i + 1 in smem1.
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const bool odd = (kt - kt0) & 1;
-    tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1);
+  // Tile kt0 + 2i lives in smem0, kt0 + 2i + 1 in smem1. Two tiles per trip,
+  // so that each tile's LDS buffers are fixed objects: every operand address is
+  // then a loop-invariant per-lane offset plus an immediate.
+  if constexpr (KD <= 32) {
+    int kt = kt0;
+    for (; kt + 1 < kt1; kt += 2) {
+      tile(kt, smem0, smem1);
+      tile(kt + 1, smem1, smem0);
+    }
+    if (kt < kt1) tile(kt, smem0, smem1);
+  } else {
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const bool odd = (kt - kt0) & 1;
+      tile(kt, odd ? smem1 : smem0, odd ? smem0 : smem1);
+    }
   }
 
   const float l_tot = l_run + lane_xor32(l_run, g);
@@ -987,7 +1001,7 @@ hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream)
 // 256 needs more than half the register file).
 template <int KD, bool kNCHW, bool kVecN>
 constexpr int occ_target() {
-  return KD > 64 ? (kNCHW ? 1 : 2) : (kNCHW && kVecN && KD == 64) ? 3 : 2;
+  return KD > 64 ? (kNCHW ? 1 : 2) : (kNCHW && kVecN && KD == 64) ? 3 : (kNCHW && kVecN && KD == 32) ? 4 : 2;
 }
 
 // NCHW tiles are staged straight into LDS with buffer loads whose offsets
