@@ -513,6 +513,7 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   const int qt = L - bh * a.q_tiles;
   const int q_row = qt * BM + wave * 32 + l32;
   const bool q_ok = q_row < a.n_q;
+  const bool wave_live = qt * BM + wave * 32 < a.n_q;   // uniform across the wave
 
   // Packed V with DV = 16: columns 16..31 of every V row stay zero in both buffers.
   if constexpr (!kNCHW && !kDirect && C::DVP > DV) {
@@ -602,98 +603,103 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
       if (more) stage.load(a, bh, kt + 1, tid);
     }
 
-    // S^T = K Q^T for the tile's keys (rows permuted by key_of_row).
-    f32x16 sacc[NKB];
+    // A wave whose 32 queries all lie past n_q (the last query tile of a
+    // batch-head when n_q is not a multiple of the tile) only helps stage
+    // the tiles and meets the barriers.
+    if (wave_live) {
+      // S^T = K Q^T for the tile's keys (rows permuted by key_of_row).
+      f32x16 sacc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        bf16x8 kop;
-        if constexpr (kNCHW)
-          kop = lds_read_tr8(ks + (ds * 16 + 8 * g + (i16 >> 2)) * C::KROW + kb * 32 + 16 * t16 +
-                                 tr_key_col(i16 & 3), C::KROW);
-        else if constexpr (kDirect) {
-          const int row = kb * 32 + key_of_row(l32);
-          kop = *reinterpret_cast<const bf16x8*>(ks + row * C::KROW + packed_chunk_pos<KD>(row, ds * 2 + g) * 8);
-        } else
-          kop = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + key_of_row(l32)) * C::KROW + ds * 16 + g * 8);
-        sacc[kb] = mfma32x32x16(kop, qop[ds], sacc[kb]);
+        for (int ds = 0; ds < NDS; ++ds) {
+          bf16x8 kop;
+          if constexpr (kNCHW)
+            kop = lds_read_tr8(ks + (ds * 16 + 8 * g + (i16 >> 2)) * C::KROW + kb * 32 + 16 * t16 +
+                                   tr_key_col(i16 & 3), C::KROW);
+          else if constexpr (kDirect) {
+            const int row = kb * 32 + key_of_row(l32);
+            kop = *reinterpret_cast<const bf16x8*>(ks + row * C::KROW + packed_chunk_pos<KD>(row, ds * 2 + g) * 8);
+          } else
+            kop = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + key_of_row(l32)) * C::KROW + ds * 16 + g * 8);
+          sacc[kb] = mfma32x32x16(kop, qop[ds], sacc[kb]);
+        }
       }
-    }
-    // Keys past n_k (last tile only) get -inf. Element r of block kb holds
-    // key 32*kb + 16*(r/8) + 8*g + r%8 of the tile.
-    if ((kt + 1) * kBN > a.n_k) {
+      // Keys past n_k (last tile only) get -inf. Element r of block kb holds
+      // key 32*kb + 16*(r/8) + 8*g + r%8 of the tile.
+      if ((kt + 1) * kBN > a.n_k) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt * kBN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+            if (key >= a.n_k) sacc[kb][r] = -INFINITY;
+          }
+      }
+
+      // Online softmax: running max, rescale, P = 2^(c*S - m).
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * kBN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (key >= a.n_k) sacc[kb][r] = -INFINITY;
-        }
-    }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      // The running max only moves when some lane's tile max exceeds it by more
+      // than 8 (log2 units): until then P <= 2^8, harmless in fp32 and bf16. The
+      // test is on the raw scores, against the threshold kept since the last move.
+      // A query's keys are split between lanes l and l ^ 32, which hold the same
+      // threshold, so testing each lane's own half decides exactly as testing the
+      // whole row would; the row max itself is only needed when the max moves.
+      if (__any(mx > m_thr)) {
+        mx = fmaxf(mx, lane_xor32(mx, g));
+        const float m_new = fmaxf(m_run, mx * a.c);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        m_thr = (m_run + 8.0f) * inv_c;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
 
-    // Online softmax: running max, rescale, P = 2^(c*S - m).
-    float mx = -INFINITY;
+      bf16x8 pop[NKS];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int s = 0; s < NKS; ++s) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    // The running max only moves when some lane's tile max exceeds it by more
-    // than 8 (log2 units): until then P <= 2^8, harmless in fp32 and bf16. The
-    // test is on the raw scores, against the threshold kept since the last move.
-    // A query's keys are split between lanes l and l ^ 32, which hold the same
-    // threshold, so testing each lane's own half decides exactly as testing the
-    // whole row would; the row max itself is only needed when the max moves.
-    if (__any(mx > m_thr)) {
-      mx = fmaxf(mx, lane_xor32(mx, g));
-      const float m_new = fmaxf(m_run, mx * a.c);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      m_thr = (m_run + 8.0f) * inv_c;
-      l_run *= alpha;
+        for (int j = 0; j < 8; ++j)
+          pop[s][j] = static_cast<__bf16>(fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -m_run)));
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const bf16x2 pp = {pop[s][j], pop[s][j + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l_run, false);
+        }
+      }
+
+      // O^T += V^T P^T: step s covers keys 16s + 8g + j of the tile in this lane's P.
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int s = 0; s < NKS; ++s) {
+          bf16x8 vop;
+          if constexpr (kDirect && kNCHW)
+            vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW +
+                                                   tile_chunk_pos(db * 32 + l32, 2 * s + g) * 8);
+          else if constexpr (kDirect) {
+            // Two transposed reads, rows r and r + 4, each at its own swizzled chunk.
+            const int r = s * 16 + 8 * g + (i16 >> 2);
+            const int col = db * 32 + 16 * t16 + 4 * (i16 & 3);
+            vop = lds_read_tr8_2(vs + r * C::VROW + packed_chunk_pos<DV>(r, col >> 3) * 8 + (col & 7),
+                                 vs + (r + 4) * C::VROW + packed_chunk_pos<DV>(r + 4, col >> 3) * 8 + (col & 7));
+          } else if constexpr (kNCHW)
+            vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW + s * 16 + g * 8);
+          else
+            vop = lds_read_tr8(vs + (s * 16 + 8 * g + (i16 >> 2)) * C::VROW + db * 32 + 16 * t16 + 4 * (i16 & 3),
+                               C::VROW);
+          oacc[db] = mfma32x32x16(vop, pop[s], oacc[db]);
+        }
     }
-
-    bf16x8 pop[NKS];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        pop[s][j] = static_cast<__bf16>(fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -m_run)));
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const bf16x2 pp = {pop[s][j], pop[s][j + 1]};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l_run, false);
-      }
-    }
-
-    // O^T += V^T P^T: step s covers keys 16s + 8g + j of the tile in this lane's P.
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        bf16x8 vop;
-        if constexpr (kDirect && kNCHW)
-          vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW +
-                                                 tile_chunk_pos(db * 32 + l32, 2 * s + g) * 8);
-        else if constexpr (kDirect) {
-          // Two transposed reads, rows r and r + 4, each at its own swizzled chunk.
-          const int r = s * 16 + 8 * g + (i16 >> 2);
-          const int col = db * 32 + 16 * t16 + 4 * (i16 & 3);
-          vop = lds_read_tr8_2(vs + r * C::VROW + packed_chunk_pos<DV>(r, col >> 3) * 8 + (col & 7),
-                               vs + (r + 4) * C::VROW + packed_chunk_pos<DV>(r + 4, col >> 3) * 8 + (col & 7));
-        } else if constexpr (kNCHW)
-          vop = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * C::VROW + s * 16 + g * 8);
-        else
-          vop = lds_read_tr8(vs + (s * 16 + 8 * g + (i16 >> 2)) * C::VROW + db * 32 + 16 * t16 + 4 * (i16 & 3),
-                             C::VROW);
-        oacc[db] = mfma32x32x16(vop, pop[s], oacc[db]);
-      }
 
     if constexpr (kDirect) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of tile kt+1 landed
