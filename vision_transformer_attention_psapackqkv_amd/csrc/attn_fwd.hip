@@ -709,10 +709,12 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     __syncthreads();
   };
 
-  // Tile kt0 + 2i lives in smem0, kt0 + 2i + 1 in smem1. Two tiles per trip,
-  // so that each tile's LDS buffers are fixed objects: every operand address is
-  // then a loop-invariant per-lane offset plus an immediate.
-  if constexpr (KD <= 32) {
+  // Tile kt0 + 2i lives in smem0, kt0 + 2i + 1 in smem1. Up to key_dim 64 the
+  // loop takes two tiles per trip, so that each tile's LDS buffers are fixed
+  // objects: every operand address is then a loop-invariant per-lane offset
+  // plus an immediate (key_dim 128 has no registers to spare for the second
+  // set of addresses).
+  if constexpr (KD <= 64) {
     int kt = kt0;
     for (; kt + 1 < kt1; kt += 2) {
       tile(kt, smem0, smem1);
