@@ -583,6 +583,20 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
   float m_thr = -INFINITY;   // (m_run + 8) / (scale*log2(e)): the rescale threshold on raw scores
   const float inv_c = 1.0f / a.c;
   float l_run = 0.0f;        // this lane's part of the running sum (its lane group's keys)
+  // At key_dim 32 the VALU work per score outweighs the MFMA work, so the row
+  // sums go to the matrix cores instead: one 16x16x32 MFMA per 16-key step
+  // multiplies a selector (row 0 picks the B rows of queries 0..15, row 1 those
+  // of queries 16..31) by the step's P operand as laid out for the PV product.
+  // Lane n < 16 then holds the running sum of query n in element 0 and of
+  // query 16 + n in element 1; every other accumulator element stays zero.
+  constexpr bool kSumMfma = KD == 32;
+  f32x4 lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8 lsel;
+  {
+    const __bf16 on = static_cast<__bf16>((lane & 15) == ((lane >> 4) & 1) ? 1.0f : 0.0f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lsel[j] = on;
+  }
 
   if constexpr (kDirect) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of tile kt0 landed
@@ -657,7 +671,12 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         m_thr = (m_run + 8.0f) * inv_c;
-        l_run *= alpha;
+        if constexpr (kSumMfma) {
+          lacc[0] *= __shfl(alpha, lane & 15);
+          lacc[1] *= __shfl(alpha, (lane & 15) + 16);
+        } else {
+          l_run *= alpha;
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -670,10 +689,14 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           pop[s][j] = static_cast<__bf16>(fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + j], a.c, -m_run)));
+        if constexpr (kSumMfma) {
+          lacc = mfma16x16x32(lsel, pop[s], lacc);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const bf16x2 pp = {pop[s][j], pop[s][j + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l_run, false);
+          for (int j = 0; j < 8; j += 2) {
+            const bf16x2 pp = {pop[s][j], pop[s][j + 1]};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l_run, false);
+          }
         }
       }
 
@@ -728,7 +751,13 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
     }
   }
 
-  const float l_tot = l_run + lane_xor32(l_run, g);
+  float l_tot;
+  if constexpr (kSumMfma) {
+    const float s0 = __shfl(lacc[0], l32 & 15), s1 = __shfl(lacc[1], l32 & 15);
+    l_tot = l32 < 16 ? s0 : s1;
+  } else {
+    l_tot = l_run + lane_xor32(l_run, g);
+  }
   store_result<DV, NDB, BM, C::PART, kNCHW>(a, oacc, m_run, l_tot, bh, q_row, q_ok, split, piece, wave * 32 + l32, g);
 }
 
