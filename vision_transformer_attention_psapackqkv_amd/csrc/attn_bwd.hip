@@ -5,10 +5,12 @@
 // grid. With P = exp(scale*Q K^T - LSE) recomputed from the forward's LSE,
 // Delta = rowsum(dO * O) and dS = P * (dO V^T - Delta):
 //   dV = P^T dO,   dK = scale * dS^T Q,   dQ = scale * dS K.
-// Three launches: Delta (one pass over O and dO; stored negated, as the dP
-// accumulators start from -Delta, beside LSE * log2(e)), dK/dV (one workgroup per
-// key tile, looping over query tiles) and dQ (one workgroup per query tile,
-// looping over key tiles). Neither uses atomics.
+// Head dims 32..128 take two launches: dQ (one workgroup per query tile,
+// looping over key tiles), which also computes Delta for its query rows from
+// the O and dO rows it loads and stores it negated (the dP accumulators start
+// from -Delta) beside LSE * log2(e), then dK/dV (one workgroup per key tile,
+// looping over query tiles), which reads both. Head dim 16 runs a separate
+// Delta pass first. Neither kernel uses atomics.
 //
 // The matrix-core products use v_mfma_f32_32x32x16_bf16 with the operand
 // placement of the forward kernel: the rows of the first products' LDS
@@ -717,20 +719,33 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
 
   // This lane's query and dO rows as B operands. Queries past n_q load row
   // n_q - 1 (all loads unconditional) and are zeroed afterwards; they are
-  // never stored.
+  // never stored. This kernel runs first and also computes, for its queries,
+  // -Delta = -rowsum(dO o O) (lanes l and l ^ 32 each hold half of a row) and
+  // LSE * log2(e), and stores both for the dK/dV kernel.
   bf16x8 qop[NDS], gop[NDS];
   float l2, dl;
   {
     const int qc = min(q, a.n_q - 1);
-    u32x4 qr[NDS], gr[NDS];
+    const int64_t row = static_cast<int64_t>(bh) * a.n_q + qc;
+    u32x4 qr[NDS], gr[NDS], orow[NDS];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      const int64_t off = (static_cast<int64_t>(bh) * a.n_q + qc) * D + ds * 16 + g * 8;
+      const int64_t off = row * D + ds * 16 + g * 8;
       qr[ds] = load16(a.q + off);
       gr[ds] = load16(a.dout + off);
+      orow[ds] = load16(a.o + off);
     }
-    const float lv = a.lse2[static_cast<int64_t>(bh) * a.n_q + qc];
-    const float dv = a.delta[static_cast<int64_t>(bh) * a.n_q + qc];
+    const float lv = a.lse[row] * kLog2e;
+    float part = 0.0f;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        part = fmaf(__builtin_bit_cast(float, orow[ds][w] << 16), __builtin_bit_cast(float, gr[ds][w] << 16), part);
+        part = fmaf(__builtin_bit_cast(float, orow[ds][w] & 0xFFFF0000u),
+                    __builtin_bit_cast(float, gr[ds][w] & 0xFFFF0000u), part);
+      }
+    const float dv = -(part + __shfl_xor(part, 32));
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       qop[ds] = as_bf16x8(q_ok ? qr[ds] : zero4());
@@ -738,6 +753,10 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
     }
     l2 = q_ok ? lv : 0.0f;
     dl = q_ok ? dv : 0.0f;
+    if (q_ok && g == 0) {
+      a.delta[row] = dv;
+      a.lse2[row] = lv;
+    }
   }
   f32x16 dq_acc[NDB];
 #pragma unroll
@@ -934,13 +953,15 @@ bool bwd_direct(int D, int n_q, int n_k) {
   return D >= 32 && n * D * 2 < (int64_t(1) << 31);
 }
 
-// The direct-staged dK/dV and dQ launches (head dims 32..128; false for 16).
+// The direct-staged dQ and dK/dV launches (head dims 32..128; false for 16).
+// The dQ kernel goes first: it also stores -Delta and LSE * log2(e), which
+// the dK/dV kernel reads.
 template <int D>
 typename std::enable_if<(D >= 32), bool>::type launch_direct(const BwdArgs& kv, dim3 grid_kv, const BwdArgs& qa,
                                                               dim3 grid_q, hipStream_t stream) {
   if (!bwd_direct(D, kv.n_q, kv.n_k)) return false;
-  bwd_dkdv_direct<D, kWavesBwd><<<grid_kv, kWavesBwd * 64, 0, stream>>>(kv);
   bwd_dq_direct<D, kWavesBwd><<<grid_q, kWavesBwd * 64, 0, stream>>>(qa);
+  bwd_dkdv_direct<D, kWavesBwd><<<grid_kv, kWavesBwd * 64, 0, stream>>>(kv);
   return true;
 }
 template <int D>
@@ -954,7 +975,6 @@ hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.BH) * a.n_q;
   const dim3 grid_delta(static_cast<unsigned>((rows + 255) / 256));
   if (bf16) {
-    bwd_delta<D, true><<<grid_delta, 256, 0, stream>>>(a);
     BwdArgs kv = a;
     kv.tiles = (a.n_k + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
     const dim3 grid_kv(static_cast<unsigned>(a.BH) * kv.tiles);
@@ -962,6 +982,7 @@ hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
     qa.tiles = (a.n_q + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
     const dim3 grid_q(static_cast<unsigned>(a.BH) * qa.tiles);
     if (launch_direct<D>(kv, grid_kv, qa, grid_q, stream)) return hipGetLastError();
+    bwd_delta<D, true><<<grid_delta, 256, 0, stream>>>(a);
     bwd_dkdv_bf16<D, kWavesBwd><<<grid_kv, kWavesBwd * 64, 0, stream>>>(kv);
     bwd_dq_bf16<D, kWavesBwd><<<grid_q, kWavesBwd * 64, 0, stream>>>(qa);
   } else {

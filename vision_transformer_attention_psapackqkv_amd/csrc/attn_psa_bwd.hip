@@ -11,10 +11,10 @@
 //   dS    = P * (dO V^T - Delta)       (one dS serves both halves)
 //   dV    = P^T dO + dV_residual,   dK = s dS^T Q,   dQ = s dS K.
 // Like the page's FA2 backward, dQ and dK/dV are separate kernels with their
-// own grids (no atomics):
-//   psa_bwd_prep: -Delta and LSE * log2(e) per (bh, pixel);
-//   psa_bwd_dkdv: one workgroup per (bh, 128 keys), looping over 64-query tiles;
-//   psa_bwd_dq:   one workgroup per (bh, 128 queries), looping over 64-key tiles.
+// own grids (no atomics), launched in this order:
+//   psa_bwd_dq:   one workgroup per (bh, 128 queries), looping over 64-key tiles;
+//                 it also stores -Delta and LSE * log2(e) for its pixels;
+//   psa_bwd_dkdv: one workgroup per (bh, 128 keys), looping over 64-query tiles.
 // Every tensor is read and written in NCHW (channel rows of N pixels), so the
 // split, pack and unpack permutations of an unfused chain never run.
 //
@@ -159,25 +159,6 @@ struct StageRegs {
     }
   }
 };
-
-// ---------------------------------------------------------------- prep
-
-template <int DV>
-__global__ __launch_bounds__(256) void psa_bwd_prep(PsaBwdArgs a) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(a.BH) * a.N) return;
-  const int64_t bh = idx / a.N;
-  const int64_t n = idx - bh * a.N;
-  const uint16_t* o = a.o + bh * DV * a.N + n;
-  const uint16_t* g = a.dout + bh * DV * a.N + n;
-  float acc = 0.0f;
-#pragma unroll 8
-  for (int dv = 0; dv < DV; ++dv)
-    acc = fmaf(bf16_bits_to_float(o[static_cast<int64_t>(dv) * a.N]),
-               bf16_bits_to_float(g[static_cast<int64_t>(dv) * a.N]), acc);
-  a.delta[idx] = -acc;   // stored negated: the dP accumulators start from it
-  a.lse2[idx] = a.lse[idx] * kLog2e;
-}
 
 // ---------------------------------------------------------------- dK / dV
 
@@ -403,25 +384,45 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
   // B operands: Q[q][16ds + 8g + j] and dO[q][16vs + 8g + j]. Queries past N
   // load pixel N - 1 (every load unconditional, all in flight together) and
   // are zeroed afterwards.
+  // This kernel runs first and also computes, for its pixels, -Delta =
+  // -rowsum(dO o O) over both halves (lanes l and l ^ 32 each hold half of the
+  // channels) and LSE * log2(e), and stores both for the dK/dV kernel.
   bf16x8 qop[NDS], gop[NVS];
   float l2, dl;
   {
     const int qc = min(q, N - 1);
-    u32x4 qr[NDS], gr[NVS];
+    const int64_t row = static_cast<int64_t>(bh) * N + qc;
+    const uint16_t* out = a.o + static_cast<int64_t>(bh) * DV * N;
+    u32x4 qr[NDS], gr[NVS], orow[NVS];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
       qr[ds] = gather8(qkv + static_cast<int64_t>(ds * 16 + g * 8) * N + qc, N, 0, 8);
 #pragma unroll
-    for (int vs = 0; vs < NVS; ++vs)
+    for (int vs = 0; vs < NVS; ++vs) {
       gr[vs] = gather8(dout + static_cast<int64_t>(vs * 16 + g * 8) * N + qc, N, 0, 8);
-    const float lv = a.lse2[static_cast<int64_t>(bh) * N + qc];
-    const float dv = a.delta[static_cast<int64_t>(bh) * N + qc];
+      orow[vs] = gather8(out + static_cast<int64_t>(vs * 16 + g * 8) * N + qc, N, 0, 8);
+    }
+    const float lv = a.lse[row] * kLog2e;
+    float part = 0.0f;
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        part = fmaf(__builtin_bit_cast(float, orow[vs][w] << 16), __builtin_bit_cast(float, gr[vs][w] << 16), part);
+        part = fmaf(__builtin_bit_cast(float, orow[vs][w] & 0xFFFF0000u),
+                    __builtin_bit_cast(float, gr[vs][w] & 0xFFFF0000u), part);
+      }
+    const float dv = -(part + __shfl_xor(part, 32));
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) qop[ds] = as_bf16x8(q_ok ? qr[ds] : zero4());
 #pragma unroll
     for (int vs = 0; vs < NVS; ++vs) gop[vs] = as_bf16x8(q_ok ? gr[vs] : zero4());
     l2 = q_ok ? lv : INFINITY;
     dl = q_ok ? dv : 0.0f;
+    if (q_ok && g == 0) {
+      a.delta[row] = dv;
+      a.lse2[row] = lv;
+    }
   }
   f32x16 dq[NDB];
 #pragma unroll
@@ -538,23 +539,21 @@ hipError_t run_psa_bwd(PsaBwdArgs a, hipStream_t stream) {
   // stay in 256 registers); key_dim 128 needs a whole SIMD's register file.
   constexpr int kOccDkdv = KD <= 32 ? 3 : KD <= 64 ? 2 : 1;
   constexpr int kOccDq = KD <= 32 ? 3 : KD <= 64 ? 2 : 1;
-  const int64_t rows = static_cast<int64_t>(a.BH) * a.N;
-  psa_bwd_prep<2 * KD><<<dim3(static_cast<unsigned>((rows + 255) / 256)), 256, 0, stream>>>(a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   a.tiles = (a.N + 32 * kWavesBwd - 1) / (32 * kWavesBwd);
   const dim3 grid(static_cast<unsigned>(a.BH) * a.tiles);
   // Direct staging addresses one batch-head's [4*KD][N] slab with 32-bit offsets.
   const bool vec_n = a.N % 8 == 0 && static_cast<int64_t>(8) * KD * a.N < (int64_t(1) << 31);
-  if (vec_n)
-    psa_bwd_dkdv<KD, true, kOccDkdv><<<grid, kThreadsBwd, 0, stream>>>(a);
-  else   // the register-staged tiles need more registers
-    psa_bwd_dkdv<KD, false, KD <= 32 ? 3 : 1><<<grid, kThreadsBwd, 0, stream>>>(a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // dQ first: it stores -Delta and LSE * log2(e), which the dK/dV kernel reads.
   if (vec_n)
     psa_bwd_dq<KD, true, kOccDq><<<grid, kThreadsBwd, 0, stream>>>(a);
   else   // the register-staged tiles need more registers
     psa_bwd_dq<KD, false, KD <= 32 ? 2 : 1><<<grid, kThreadsBwd, 0, stream>>>(a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (vec_n)
+    psa_bwd_dkdv<KD, true, kOccDkdv><<<grid, kThreadsBwd, 0, stream>>>(a);
+  else   // the register-staged tiles need more registers
+    psa_bwd_dkdv<KD, false, KD <= 32 ? 3 : 1><<<grid, kThreadsBwd, 0, stream>>>(a);
   return hipGetLastError();
 }
 
