@@ -155,11 +155,15 @@ def test_psa_fused_repeatable_and_matches_halves():
 # key_dim 32 at batch 8): given a workspace, the launch cuts those last query
 # tiles into key-range pieces and merges them in a second kernel. Checked on
 # the first head and the last two (whose tiles are all in the last round),
-# every query row, and against the same launch run unsplit.
+# every query row, and against the same launch run unsplit. The 44x48 maps
+# (N = 2112, 16.5 query tiles per batch-head) put a half-empty query tile, whose
+# last two waves hold no query, among the split tiles of the last batch-head.
 TAIL_PSA = [
     (2, 8, 64, 80, 80),
     (4, 4, 128, 80, 80),
     (8, 8, 32, 48, 48),
+    (8, 8, 32, 44, 48),
+    (12, 8, 64, 44, 48),
 ]
 
 
@@ -193,12 +197,14 @@ def test_psa_fused_tail_split(shape):
     assert (l_none - lse).abs().max().item() < 1e-3
 
 
-def test_fa2_fwd_tail_split():
-    """FA2 forward on packed [BH, n, D] tensors whose grid leaves a short last round
-    (BH = 32, n = 6400, D = 64), checked on the last two batch-heads."""
+@pytest.mark.parametrize("shape", [(32, 6400, 64), (48, 2112, 64)], ids=lambda s: "BH{}n{}d{}".format(*s))
+def test_fa2_fwd_tail_split(shape):
+    """FA2 forward on packed [BH, n, D] tensors whose grid leaves a short last round,
+    checked on the last two batch-heads (n = 2112: a half-empty last query tile among
+    the split tiles)."""
     dev = device()
-    BH, n, D = 32, 6400, 64
-    announce("fa2_fwd tail split BH32 n6400 d64")
+    BH, n, D = shape
+    announce(f"fa2_fwd tail split BH{BH} n{n} d{D}")
     assert psa.fa2_fwd_workspace_bytes(BH, n, n, D) > 0
     q, k, v = I.make_attention_inputs(BH, n, n, D, seed=31)
     o, lse = psa.fa2_fwd(q.to(dev), k.to(dev), v.to(dev))
