@@ -655,6 +655,18 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of the next tile landed
     __syncthreads();
   };
+  // A wave whose 32 keys all lie past n_k (the last key tile of a batch-head
+  // when n_k is not a multiple of 128) only helps stage the tiles and meets
+  // the barriers, in a loop of its own (a branch inside the loop below would
+  // cost it registers).
+  if (kt * 32 * kWaves + wave * 32 >= a.n_k) {
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) issue(t + 1, (t & 1) ? smem0 : smem1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    return;
+  }
   // Tile t lives in smem0 for even t, smem1 for odd. Two tiles per trip, so
   // that each one reads a fixed LDS object: every LDS address is then a
   // loop-invariant per-lane offset plus a constant.
@@ -686,7 +698,7 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
 }
 
 template <int D, int kWaves>
-__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bwd_dq_direct(BwdArgs a) {
+__global__ __launch_bounds__(kWaves * 64, D <= 32 ? 4 : D == 64 ? 2 : 1) void bwd_dq_direct(BwdArgs a) {
   constexpr int BN = 64;                 // keys per tile
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
@@ -805,6 +817,16 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of the next tile landed
     __syncthreads();
   };
+  // A wave whose 32 queries all lie past n_q only helps stage the tiles, as in
+  // the dK/dV kernel.
+  if (qt * BM + wave * 32 >= a.n_q) {
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) issue(t + 1, (t & 1) ? smem0 : smem1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    return;
+  }
   int kt = 0;   // two tiles per trip, as in the dK/dV kernel
   for (; kt + 1 < n_tiles; kt += 2) {
     tile(kt, smem0, smem1);

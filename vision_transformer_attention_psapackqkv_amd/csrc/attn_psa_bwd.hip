@@ -322,6 +322,21 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dkdv(PsaBwdArgs a) 
     if (more) finish(nbuf);
     __syncthreads();
   };
+  // A wave whose 32 keys all lie past N (the last key tile of a batch-head when
+  // N is not a multiple of 128) only helps stage the tiles and meets the
+  // barriers, in a loop of its own (a branch inside the loop below would cost
+  // it registers).
+  if (kt * 32 * kWavesBwd + wave * 32 >= N) {
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) {
+        uint16_t* nb = (t & 1) ? smem0 : smem1;
+        issue(t + 1, nb);
+        finish(nb);
+      }
+      __syncthreads();
+    }
+    return;
+  }
   for (int qt = 0; qt < n_tiles; ++qt) {   // tile t lives in smem0 for even t, smem1 for odd
     const bool odd = qt & 1;
     tile(qt, odd ? smem1 : smem0, odd ? smem0 : smem1);
@@ -504,6 +519,19 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
     if (more) finish(nbuf);
     __syncthreads();
   };
+  // A wave whose 32 queries all lie past N only helps stage the tiles, as in
+  // the dK/dV kernel.
+  if (qt * 32 * kWavesBwd + wave * 32 >= N) {
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) {
+        uint16_t* nb = (t & 1) ? smem0 : smem1;
+        issue(t + 1, nb);
+        finish(nb);
+      }
+      __syncthreads();
+    }
+    return;
+  }
   // Tile t lives in smem0 for even t, smem1 for odd. Two tiles per trip, so
   // that each reads a fixed LDS object and every LDS address is a
   // loop-invariant per-lane offset plus a constant (-1.1 % on the 40x40 map;
