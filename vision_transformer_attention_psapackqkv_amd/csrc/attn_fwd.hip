@@ -111,6 +111,13 @@ __device__ __forceinline__ float lane_xor32(float x, int g) {
   return __builtin_bit_cast(float, g ? sw[0] : sw[1]);
 }
 
+// Position of 16-byte chunk c of K channel row `row` in a directly staged
+// NCHW key tile (64 keys = 8 chunks per row). The transposed K reads of one
+// 32-lane half take chunks 4kb..4kb+3 of four consecutive rows; flipping
+// chunk bit 2 on rows 2 and 3 of every four puts those 256 bytes on all 64
+// banks (unswizzled, rows r and r + 2 share their banks).
+__device__ __forceinline__ int k_chunk_pos(int row, int c) { return c ^ (((row >> 1) & 1) << 2); }
+
 // Whether a kernel instance stages its tiles straight into LDS: NCHW tiles
 // with N a multiple of 8, packed tiles with head dim 32..128 (kVecN then means
 // the rows fit the buffer offsets).
@@ -163,11 +170,12 @@ struct FwdStageDirect {
 
   // Block b covers 8 channel rows starting at chan0(b) of the batch-head's
   // [4*KD][N] slab; lane i fills LDS chunk i of it: row i/8 of the block, and
-  // the 8 keys the swizzle puts at position i%8.
+  // the 8 keys the swizzle puts at position i%8 (k_chunk_pos for K rows,
+  // tile_chunk_pos for V rows; both are their own inverses).
   __device__ static int chan0(int b) { return b < K_BLOCKS ? KD + 8 * b : 2 * KD + 8 * (b - K_BLOCKS); }
   __device__ static int chunk(int b, int lane) {
     const int r = lane >> 3;
-    return b < K_BLOCKS ? (lane & 7) : tile_chunk_pos(8 * (b - K_BLOCKS) + r, lane & 7);
+    return b < K_BLOCKS ? k_chunk_pos(8 * b + r, lane & 7) : tile_chunk_pos(8 * (b - K_BLOCKS) + r, lane & 7);
   }
 
   uint32_t voff[PER];   // byte offset of this lane's 16 bytes from the block's (row, key) origin
@@ -630,7 +638,12 @@ __global__ __launch_bounds__(kWaves * 64, kOcc) void attn_fwd_bf16(FwdArgs a) {
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
           bf16x8 kop;
-          if constexpr (kNCHW)
+          if constexpr (kNCHW && kDirect) {
+            // Rows row and row + 4 of the two reads share the swizzle.
+            const int row = ds * 16 + 8 * g + (i16 >> 2);
+            const int col = kb * 32 + 16 * t16 + tr_key_col(i16 & 3);
+            kop = lds_read_tr8(ks + row * C::KROW + k_chunk_pos(row, col >> 3) * 8 + (col & 7), C::KROW);
+          } else if constexpr (kNCHW)
             kop = lds_read_tr8(ks + (ds * 16 + 8 * g + (i16 >> 2)) * C::KROW + kb * 32 + 16 * t16 +
                                    tr_key_col(i16 & 3), C::KROW);
           else if constexpr (kDirect) {
