@@ -98,9 +98,16 @@ __device__ __forceinline__ int key_of_row(int rho) {
 __device__ __forceinline__ int tr_key_col(int s) { return ((s & 1) << 3) | ((s & 2) << 1); }
 
 // Position of 16-byte chunk c of row `row` in an unpadded LDS tile of 64
-// bf16 columns: an XOR swizzle that puts the 16 rows one 16-byte-per-lane
-// instruction reads together on 16 different bank groups.
-__device__ __forceinline__ int tile_chunk_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
+// bf16 columns: an XOR swizzle with x = (row >> 1) & 7 mapped to
+// ((x & 1) << 2) | (x >> 1). The map is a bijection of 0..7, so the 16 rows
+// one 16-byte-per-lane instruction reads together fall on 16 different bank
+// groups; and rows 4k + 2, 4k + 3 flip chunk bit 2 against rows 4k, 4k + 1, so
+// a transposed read of chunks 4j..4j+3 of four consecutive rows (one 32-lane
+// half of ds_read_b64_tr_b16) covers all 64 banks once.
+__device__ __forceinline__ int tile_chunk_pos(int row, int c) {
+  const int x = (row >> 1) & 7;
+  return c ^ (((x & 1) << 2) | (x >> 1));
+}
 
 // Position of 16-byte chunk c of row `row` in an unpadded tile of packed rows
 // of D columns (D/8 chunks per row): an XOR swizzle chosen so that neither the
