@@ -850,21 +850,29 @@ constexpr int kF32Threads = 128;
 constexpr int kF32Keys = 32;
 
 // One thread per query row, keys staged through LDS in tiles of 32, float32
-// throughout with expf. Workgroups enumerate (bh, V half, query block); the
-// fused (NCHW) variant has two V halves, the packed variant one.
+// throughout with expf. The fused (NCHW) variant computes the softmax once and
+// multiplies P by both V halves, [V_lo | V_hi] (value width 2*KD), as the bf16
+// kernel does, up to key_dim 64; at key_dim 128 (a 256-wide accumulator per
+// thread would not fit the registers) workgroups take one V half each and the
+// softmax is computed once per half. Workgroups enumerate (bh, V part, query
+// block).
+template <int KD, bool kNCHW>
+constexpr int f32_parts() { return kNCHW && KD > 64 ? 2 : 1; }   // workgroups per (bh, query block)
+
 template <int KD, bool kNCHW>
 __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
+  constexpr int kParts = f32_parts<KD, kNCHW>();
+  constexpr int VW = kNCHW && kParts == 1 ? 2 * KD : KD;   // value columns per workgroup
   __shared__ float ks[kF32Keys][KD];
-  __shared__ float vs[kF32Keys][KD];
-  const int halves = kNCHW ? 2 : 1;
+  __shared__ float vs[kF32Keys][VW];
   const int q_blocks = (a.n_q + kF32Threads - 1) / kF32Threads;
   const int qb = blockIdx.x % q_blocks;
-  const int bh = (blockIdx.x / q_blocks) / halves;
-  const int j = (blockIdx.x / q_blocks) % halves;
+  const int bh = (blockIdx.x / q_blocks) / kParts;
+  const int j = (blockIdx.x / q_blocks) % kParts;
   const int row = qb * kF32Threads + threadIdx.x;
   const bool ok = row < a.n_q;
   const int N = a.n_k;
-  // Element (row n, column d) of Q, K and V half j, in either layout.
+  // Element (row n, column d) of Q, K and this workgroup's V columns, in either layout.
   auto qi = [&](int n, int d) -> int64_t {
     return kNCHW ? (static_cast<int64_t>(bh) * 4 * KD + d) * N + n
                  : (static_cast<int64_t>(bh) * a.n_q + n) * KD + d;
@@ -874,24 +882,26 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
                  : (static_cast<int64_t>(bh) * a.n_k + n) * KD + d;
   };
   auto vi = [&](int n, int d) -> int64_t {
-    return kNCHW ? (static_cast<int64_t>(bh) * 4 * KD + (2 + j) * KD + d) * N + n
+    return kNCHW ? (static_cast<int64_t>(bh) * 4 * KD + 2 * KD + j * KD + d) * N + n
                  : (static_cast<int64_t>(bh) * a.n_k + n) * KD + d;
   };
-  float q[KD], o[KD];
+  float q[KD], o[VW];
 #pragma unroll
-  for (int d = 0; d < KD; ++d) {
-    q[d] = ok ? a.q[qi(row, d)] : 0.0f;
-    o[d] = 0.0f;
-  }
+  for (int d = 0; d < KD; ++d) q[d] = ok ? a.q[qi(row, d)] : 0.0f;
+#pragma unroll
+  for (int d = 0; d < VW; ++d) o[d] = 0.0f;
   float m = -INFINITY, l = 0.0f;
   for (int m0 = 0; m0 < a.n_k; m0 += kF32Keys) {
     __syncthreads();
     for (int e = threadIdx.x; e < kF32Keys * KD; e += kF32Threads) {
       const int r = kNCHW ? e % kF32Keys : e / KD;
       const int d = kNCHW ? e / kF32Keys : e % KD;
-      const bool in = m0 + r < a.n_k;
-      ks[r][d] = in ? a.k[ki(m0 + r, d)] : 0.0f;
-      vs[r][d] = in ? a.v[vi(m0 + r, d)] : 0.0f;
+      ks[r][d] = m0 + r < a.n_k ? a.k[ki(m0 + r, d)] : 0.0f;
+    }
+    for (int e = threadIdx.x; e < kF32Keys * VW; e += kF32Threads) {
+      const int r = kNCHW ? e % kF32Keys : e / VW;
+      const int d = kNCHW ? e / kF32Keys : e % VW;
+      vs[r][d] = m0 + r < a.n_k ? a.v[vi(m0 + r, d)] : 0.0f;
     }
     __syncthreads();
     const int cnt = min(kF32Keys, a.n_k - m0);
@@ -905,14 +915,14 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
       const float p = expf(s - m_new);
       l = l * alpha + p;
 #pragma unroll
-      for (int d = 0; d < KD; ++d) o[d] = fmaf(p, vs[r][d], o[d] * alpha);
+      for (int d = 0; d < VW; ++d) o[d] = fmaf(p, vs[r][d], o[d] * alpha);
       m = m_new;
     }
   }
   if (!ok) return;
   const float inv = 1.0f / l;
 #pragma unroll
-  for (int d = 0; d < KD; ++d) {
+  for (int d = 0; d < VW; ++d) {
     const int64_t oi = kNCHW ? (static_cast<int64_t>(bh) * 2 * KD + j * KD + d) * N + row
                              : (static_cast<int64_t>(bh) * a.n_q + row) * KD + d;
     a.o[oi] = o[d] * inv;
@@ -1083,7 +1093,7 @@ size_t split_bytes(int BH, int n_q, int n_k, bool vec_n) {
 template <int KD, bool kNCHW>
 hipError_t run_f32(FwdArgsF32 a, hipStream_t stream) {
   const unsigned q_blocks = (a.n_q + kF32Threads - 1) / kF32Threads;
-  const dim3 grid(q_blocks * a.BH * (kNCHW ? 2 : 1));
+  const dim3 grid(q_blocks * a.BH * f32_parts<KD, kNCHW>());
   attn_fwd_f32<KD, kNCHW><<<grid, kF32Threads, 0, stream>>>(a);
   return hipGetLastError();
 }
