@@ -1054,9 +1054,10 @@ hipError_t launch_bf16(FwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream)
   return hipGetLastError();
 }
 
-// Workgroups per CU the registers must allow for head dims up to 64: three
-// where the LDS also holds three (directly staged NCHW tiles, key_dim 64),
-// else two. Head dim 128: two for fa2_fwd (220 VGPRs, no spills; with no cap
+// Workgroups per CU the registers must allow for head dims up to 64: four for
+// directly staged NCHW tiles at key_dim 32 (whose 24 KB of LDS allow four;
+// the two-tile loop would otherwise take 130 VGPRs), three for them at key_dim
+// 64 (48 KB of LDS), else two. Head dim 128: two for fa2_fwd (220 VGPRs, no spills; with no cap
 // the compiler took 296 and ran one), one for the fused kernel (value width
 // 256 needs more than half the register file).
 template <int KD, bool kNCHW, bool kVecN>
