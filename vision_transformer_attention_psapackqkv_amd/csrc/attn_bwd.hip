@@ -697,6 +697,8 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 3 : D == 64 ? 2 : 1) void bw
     }
 }
 
+// Registers capped for four workgroups per CU at head dim 32 (128 VGPRs, no
+// spills; left free, the compiler takes 131 and the kernel runs three).
 template <int D, int kWaves>
 __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 4 : D == 64 ? 2 : 1) void bwd_dq_direct(BwdArgs a) {
   constexpr int BN = 64;                 // keys per tile
