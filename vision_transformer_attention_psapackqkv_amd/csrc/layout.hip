@@ -9,7 +9,7 @@
 // with a slab-index permutation, and each is bound by HBM bandwidth.
 //
 // A workgroup (256 threads for pack, 512 for merge and extract) moves one
-// tile of a slab (all KD channels x 16 KB / (KD * elt) pixels) through LDS:
+// tile of a slab (all KD channels x tile_bytes / (KD * elt) pixels) through LDS:
 // 16-byte loads along the side the data is contiguous on, the transpose
 // between LDS and registers, 16-byte stores along the other side, so that
 // every wave instruction reads or writes 1 KB of contiguous runs
@@ -49,7 +49,7 @@ __device__ __forceinline__ void slab_offsets(const SlabGeom& g, int t, int64_t& 
   rows_off = (static_cast<int64_t>(g.slot0 + s) * g.BH + bh) * slab;
 }
 
-// One tile = all KD channels x PX pixels of one slab (16 KB of data), staged in
+// One tile = all KD channels x PX pixels of one slab (tile_bytes of data), staged in
 // LDS so that both global sides move in long contiguous runs: 16-byte chunk q
 // of the NCHW side is (row q / CPR, column q % CPR), so one wave instruction
 // covers 1 KB of whole channel-row runs; chunk q of the packed side is (pixel
@@ -59,9 +59,14 @@ __device__ __forceinline__ void slab_offsets(const SlabGeom& g, int t, int64_t& 
 // chunk does not run along. LDS chunk columns are XOR-swizzled by the row's
 // channel block, so the 8 rows (4 for f32) one packed-side chunk gathers from
 // sit in different bank groups.
-constexpr int kTileBytes = 16384;
-// Workgroup size: 256 threads for pack, 512 for merge and extract (measured
-// best for each direction on MI355X at the 80x80 map; 4 and 2 chunks per thread).
+// Tile bytes and workgroup size, measured best for each direction on MI355X at
+// the 80x80 map: pack moves 16 KB tiles with 256 threads (4 chunks per
+// thread); merge and extract move 8 KB tiles with 512 threads (one chunk per
+// thread; 16 KB at key_dim 128, whose 8 KB tile would have fewer than 8
+// chunks per channel row), which with their sc0 nt sc1 stores measured 1.5-2 %
+// faster than 16 KB tiles.
+template <bool kToRows, int KD>
+constexpr int tile_bytes() { return kToRows || KD >= 128 ? 16384 : 8192; }
 template <bool kToRows>
 constexpr int threads_lds() { return kToRows ? 256 : 512; }
 
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(kThreadsLds) void transpose_slabs_lds(const void* _
                                                                    SlabGeom g, int tiles_per_slab) {
   using T = typename Word<kElt>::T;
   constexpr int VEC = 16 / kElt;                 // elements per 16-byte chunk
-  constexpr int PX = kTileBytes / (KD * kElt);   // pixels per tile
+  constexpr int PX = tile_bytes<kToRows, KD>() / (KD * kElt);   // pixels per tile
   constexpr int CPR = PX / VEC;                  // chunks per channel row of a tile (>= 8)
   constexpr int DBN = KD / VEC;                  // chunks per packed row
   constexpr int PER = KD * CPR / kThreadsLds;    // chunks per thread
@@ -155,8 +160,8 @@ __global__ __launch_bounds__(kThreadsLds) void transpose_slabs_lds(const void* _
     // NCHW-side stores as buffer stores over the slab (under 2 GB: the
     // launcher checks) with the non-temporal and both scope bits set (sc0 nt
     // sc1): measured 1-1.5 % faster than plain non-temporal stores at the
-    // 80x80 map, while the same bits on the loads, or on pack's stores, were
-    // not faster.
+    // 80x80 map (with 16 KB tiles), while the same bits on the loads, or on
+    // pack's stores, were not faster.
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(dst + nchw_off, 0, KD * g.N * kElt, kBufferWord3);
 #pragma unroll
@@ -194,7 +199,7 @@ template <int kElt, bool kToRows>
 void launch_lds(const void* src, void* dst, SlabGeom g, int n_slabs, hipStream_t stream) {
   auto go = [&](auto kd) {
     constexpr int KD = decltype(kd)::value;
-    constexpr int PX = kTileBytes / (KD * kElt);
+    constexpr int PX = tile_bytes<kToRows, KD>() / (KD * kElt);
     const int tiles = (g.N + PX - 1) / PX;
     const dim3 grid(static_cast<unsigned>(n_slabs) * tiles);
     transpose_slabs_lds<kElt, KD, kToRows><<<grid, threads_lds<kToRows>(), 0, stream>>>(src, dst, g, tiles);
