@@ -436,7 +436,26 @@ def components(torch, psa, I, w, qkv, args):
     comp["fa2_bwd_40x40"] = fa2_bwd_component(torch, psa, I, dev, steps, warm)
     comp["psa_bwd_40x40"] = psa_bwd_component(torch, psa, I, dev, steps, warm)
     comp.update(yolo_components(torch, psa, dev, steps, warm))
+    comp["reference_torch_bf16_gemm_8192"] = reference_gemm(torch, dev, steps)
     return comp
+
+
+def reference_gemm(torch, dev, steps):
+    """torch's bf16 GEMM (the vendor BLAS) on 8192^3, back to back on the same box: what a
+    library contraction reaches here, as context for the attention rates (boxes differ in the
+    clock they hold under MFMA load by up to ~10 %)."""
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(3)
+    a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    fn = lambda _i: torch.mm(a, b, out=c)
+    settle(fn, torch, max_s=1.0)
+    t = back_to_back(fn, max(10, steps // 4), torch)
+    tf = 2.0 * n ** 3 / (t * 1e-3) / 1e12
+    del a, b, c
+    return {"avg_ms": round(t, 5), "TFLOP/s": round(tf, 3), "pct_bf16_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "note": "torch.mm bf16 8192x8192x8192, launches back to back; not part of the PSA path"}
 
 
 def time_graph(fns, steps, warm, torch):
