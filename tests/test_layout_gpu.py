@@ -26,7 +26,8 @@ SHAPES = [
     (1, 1, 128, 9, 7, "f32"),
     (2, 2, 64, 16, 16, "bf16"),
     # N a multiple of 8 (4 for f32) but not of the staged tile's pixel count
-    # (16 KB / (key_dim * element size)): several tiles and a short last one.
+    # (tile bytes / (key_dim * element size); 16 KB tiles for pack, 8 KB for
+    # merge and extract below key_dim 128): several tiles and a short last one.
     (2, 1, 128, 8, 10, "bf16"),
     (1, 2, 128, 12, 12, "f32"),
     (2, 2, 16, 24, 24, "bf16"),
