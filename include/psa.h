@@ -3,7 +3,7 @@
  *
  * The path (vision-rs book, "Custom Kernels", section "Position-Sensitive
  * Attention (PSA)"): a QKV convolution's NCHW output [B, qkv_h, H, W], whose
- * channels are grouped per head as [Q | K | V_lo | V_hi] (each KEY_DIM wide),
+ * channels come in per-head groups ordered Q, K, V_lo, V_hi (KEY_DIM apiece),
  * is repacked to [4, BH, N, KEY_DIM]; Flash Attention 2 runs once per V half
  * with HEAD_DIM = KEY_DIM, sharing Q and K; the two outputs are merged back to
  * NCHW [B, c, H, W]; the two V halves are also returned to NCHW, where the
@@ -81,8 +81,8 @@ psa_status psa_pack_qkv(const void* qkv_nchw, void* packed, int B, int heads, in
                         int H, int W, psa_dtype dtype, void* stream);
 
 /*
- * PsaExtractV (same page and section, PsaExtractV: the V section back out in
- * NCHW for the residual path):
+ * PsaExtractV (same page and section, PsaExtractV bullet: both V channel
+ * groups returned to NCHW, where the block's residual branch reads them):
  *   v_nchw[b][i*2*KD + j*KD + d][y][x] = packed[2+j][b*h+i][n][d]
  * packed: [4, B*h, H*W, KD] input (only slots 2 and 3 are read).
  * v_nchw: [B, 2*h*KD, H, W] output. Bit copy.
@@ -91,8 +91,8 @@ psa_status psa_extract_v(const void* packed, void* v_nchw, int B, int heads, int
                          int H, int W, psa_dtype dtype, void* stream);
 
 /*
- * PsaMergeAttn (same page and section, PsaMergeAttn: attention output back
- * into NCHW [B, c, H, W]):
+ * PsaMergeAttn (same page and section, PsaMergeAttn bullet: the two FA2
+ * outputs returned to the NCHW layout [B, c, H, W]):
  *   out_nchw[b][i*2*KD + j*KD + d][y][x] = o2[j][b*h+i][n][d]
  * o2: [2, B*h, H*W, KD] input (half 0 = attention over V_lo, 1 = over V_hi).
  * out_nchw: [B, 2*h*KD, H, W] output. Bit copy.

@@ -8,10 +8,9 @@ library, and the HIP library never falls back to it.
 What it follows (all citations are to the pages the method is described on):
 
 * vision-rs book, "Custom Kernels", section "Position-Sensitive Attention
-  (PSA)": PsaPackQkv takes the NCHW output ``[B, qkv_h, H, W]`` of a QKV
-  convolution whose channels are grouped per head as ``[Q | K | V_lo | V_hi]``,
-  each KEY_DIM wide, and produces the ``[4, BH, N, KEY_DIM]`` layout Flash
-  Attention 2 reads; PsaExtractV returns the two V sections to NCHW, where the
+  (PSA)": PsaPackQkv reorders the NCHW output ``[B, qkv_h, H, W]`` of a QKV
+  convolution, whose channels come in per-head groups ordered Q, K, V_lo,
+  V_hi (KEY_DIM apiece), into ``[4, BH, N, KEY_DIM]``, the tensors FA2 takes; PsaExtractV returns the two V sections to NCHW, where the
   block's residual branch uses them; PsaMergeAttn writes the attention output back to NCHW
   ``[B, c, H, W]``. Flash Attention 2 runs once per V half with
   HEAD_DIM = KEY_DIM, sharing Q and K.
@@ -92,7 +91,7 @@ def merge_attn(o2: np.ndarray, B: int, heads: int, key_dim: int, H: int, W: int)
     """PsaMergeAttn: ``out[b, i*2*KD + j*KD + d, y, x] = o2[j, b*heads+i, n, d]``.
 
     vision-rs book, "Custom Kernels", "Position-Sensitive Attention (PSA)",
-    PsaMergeAttn bullet: the two FA2 outputs (lo, hi) back into NCHW
+    PsaMergeAttn bullet: the two FA2 outputs (lo, hi) returned to NCHW
     ``[B, c, H, W]`` with c = 2*heads*KEY_DIM.
     """
     KD, N, BH, C = key_dim, H * W, B * heads, 2 * heads * key_dim

@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE ONLY, like psa_oracle: only the tests, ``__graft_entry__.smo
 and ``bench.py``'s ``cpu_baseline`` leg may use it; it shares no code with the HIP
 library, and the library never falls back to it.
 
-What it follows: vision-rs book, "Custom Kernels", section "Detect-decode" (raw
-LTRB box predictions plus a precomputed anchor grid, decoded to [cx, cy, w, h] in
-one pass; the anchor grid is anchor_x, anchor_y and strides, one value per
+What it follows: vision-rs book, "Custom Kernels", section "Detect-decode" (the
+head's LTRB distances and an anchor grid computed beforehand, turned into
+[cx, cy, w, h] boxes in one pass; the anchor grid is anchor_x, anchor_y and strides, one value per
 anchor) and section "Loss kernels", ``ciou`` bullet (predicted and target
 [4, N] XYWH boxes in, per-anchor loss plus the iou, v and alpha the backward
 needs out). The teenygrad book, "Your Kernel as a Graph Op", shows the decode's
