@@ -130,6 +130,55 @@ def make_workload_bwd(w: PsaWorkload):
                                  seed=w.seed, with_dout=True)
 
 
+# Score ramps: query and key rows built so that the dot product q_n . k_m grows
+# (even n) or falls (odd n) linearly along the key index m, by score_step per key,
+# plus a little N(0, noise^2) on every element (no exact ties). With u the unit
+# vector of ones / sqrt(dim): q_n = 8 * (+-1) * u + noise, k_m = (m * score_step / 8) * u
+# + noise. V is N(0, 1); dO is N(0, dout_scale^2) (the rising queries all put their
+# weight on the last keys, so dK and dV sum many dO rows).
+_RAMP_Q = 8.0
+
+
+def _ramp_qk(rng: np.random.Generator, lead, n_q: int, n_k: int, dim: int, score_step: float,
+             noise: float):
+    u = np.full(dim, 1.0 / np.sqrt(dim), dtype=np.float32)
+    sign = np.where(np.arange(n_q) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    t = np.arange(n_k, dtype=np.float32) * np.float32(score_step / _RAMP_Q)
+    q = np.float32(_RAMP_Q) * sign[:, None] * u[None, :] + np.float32(noise) * rng.standard_normal(
+        tuple(lead) + (n_q, dim), dtype=np.float32)
+    k = t[:, None] * u[None, :] + np.float32(noise) * rng.standard_normal(tuple(lead) + (n_k, dim), dtype=np.float32)
+    return q, k
+
+
+def make_ramp_attention_inputs(BH: int, n_q: int, n_k: int, head_dim: int, *, score_step: float,
+                               seed: int = 0, noise: float = 0.05, with_dout: bool = False,
+                               dout_scale: float = 0.25):
+    """bf16 Q ``[BH,n_q,D]`` and K ``[BH,n_k,D]`` on a score ramp (see above), V ``[BH,n_k,D]``
+    drawn N(0, 1) and dO ``[BH,n_q,D]`` N(0, dout_scale^2)."""
+    rng = np.random.default_rng(seed)
+    q, k = _ramp_qk(rng, (BH,), n_q, n_k, head_dim, score_step, noise)
+    v = rng.standard_normal((BH, n_k, head_dim), dtype=np.float32)
+    out = [_store(q, "bf16"), _store(k, "bf16"), _store(v, "bf16")]
+    if with_dout:
+        out.append(_store(np.float32(dout_scale) * rng.standard_normal((BH, n_q, head_dim), dtype=np.float32),
+                          "bf16"))
+    return tuple(out)
+
+
+def make_ramp_qkv(B: int, heads: int, key_dim: int, H: int, W: int, *, score_step: float,
+                  seed: int = 0, noise: float = 0.05) -> torch.Tensor:
+    """bf16 NCHW QKV-conv output ``[B, 4*heads*key_dim, H, W]`` whose query and key channels
+    (the first and second key_dim channels of each head's group) hold a score ramp over the
+    pixel index; the V channels are N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    N = H * W
+    x = rng.standard_normal((B, heads, 4, key_dim, N), dtype=np.float32)
+    q, k = _ramp_qk(rng, (B, heads), N, N, key_dim, score_step, noise)   # [B, heads, N, KD]
+    x[:, :, 0] = np.swapaxes(q, -1, -2)
+    x[:, :, 1] = np.swapaxes(k, -1, -2)
+    return _store(x.reshape(B, 4 * heads * key_dim, H, W), "bf16")
+
+
 def as_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a stored f32/bf16 tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()

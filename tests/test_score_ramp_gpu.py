@@ -1,0 +1,118 @@
+"""Inputs whose scores climb by more than the rescale threshold on every key tile.
+
+The forward kernels keep a running maximum per query and move it (rescaling O and the
+row sum) only when a key tile's scores exceed it by more than 8 in log2 units; on N(0, 1)
+inputs that happens on the first tile or two and never again. Here each even query's
+scores rise along the key index by 12 log2 units per 64-key tile (so its maximum moves on
+every tile, and split-tail pieces of one query end with running maxima hundreds of units
+apart), while each odd query's scores fall (its maximum is set once), so the waves' votes
+mix lanes that need the move with lanes that do not. Forward, tail split, FA2 backward
+and PSA backward are checked against the float64 oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import psa_inputs as I
+import vision_transformer_attention_psapackqkv_amd as psa
+from oracle import psa_oracle as O
+from tests.gpu_helpers import announce, assert_attention_close, assert_lse_close, bits, device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+LOG2_PER_TILE = 12.0   # log2 units the rising queries' scores climb per 64-key tile
+
+
+def _step(key_dim: int) -> float:
+    """Raw score increase per key for LOG2_PER_TILE log2 units per 64 keys at scale key_dim^-1/2."""
+    return LOG2_PER_TILE / (64.0 * key_dim ** -0.5 * math.log2(math.e))
+
+
+def _psa_id(s):
+    return "B{}h{}kd{}_{}x{}".format(*s)
+
+
+def _check_psa_heads(qkv, B, h, KD, H, W, out, vres, lse, sel):
+    x = to_f64(qkv)
+    packed = O.pack_qkv(x, B, h, KD, H, W)
+    s = O.default_scale(KD)
+    o_lo, want_lse = O.attention(packed[0][sel], packed[1][sel], packed[2][sel], s)
+    o_hi, _ = O.attention(packed[0][sel], packed[1][sel], packed[3][sel], s)
+    want = np.concatenate([o_lo, o_hi], axis=2)                              # [S, N, 2KD]
+    got = to_f64(out).reshape(B * h, 2 * KD, H * W)[sel].transpose(0, 2, 1)
+    assert_attention_close(got, want, "bf16", "ramp psa_attention_fwd out")
+    assert_lse_close(to_f64(lse)[sel], want_lse, "bf16", "ramp psa_attention_fwd")
+    want_v = O.extract_v(O.pack_qkv(bits(qkv), B, h, KD, H, W), B, h, KD, H, W)
+    assert np.array_equal(bits(vres), want_v), "V residual differs"
+
+
+@pytest.mark.parametrize("shape", [(2, 2, 64, 32, 32), (2, 2, 32, 24, 24), (1, 1, 128, 16, 16),
+                                   (1, 2, 16, 16, 16), (1, 1, 32, 7, 9)], ids=_psa_id)
+def test_ramp_psa_fused_fwd(shape):
+    dev = device()
+    B, h, KD, H, W = shape
+    announce(f"ramp psa_attention_fwd {_psa_id(shape)}")
+    qkv = I.make_ramp_qkv(B, h, KD, H, W, score_step=_step(KD), seed=300 + KD + H * W)
+    out, vres, lse = psa.psa_attention_fwd(qkv.to(dev), h, KD)
+    _check_psa_heads(qkv, B, h, KD, H, W, out, vres, lse, np.arange(B * h))
+
+
+@pytest.mark.parametrize("shape", [(8, 8, 32, 48, 48), (2, 8, 64, 80, 80)], ids=_psa_id)
+def test_ramp_psa_tail_split(shape):
+    """Grids whose last round is cut into key-range pieces: a rising query's pieces end with
+    running maxima far apart, so the merge's weights span many orders of magnitude."""
+    dev = device()
+    B, h, KD, H, W = shape
+    announce(f"ramp psa_attention_fwd tail split {_psa_id(shape)}")
+    nbytes = psa.psa_attention_fwd_workspace_bytes(B, h, KD, H, W)
+    assert nbytes > 0, "this grid is expected to split its last round on a 256-CU gfx950"
+    qkv = I.make_ramp_qkv(B, h, KD, H, W, score_step=_step(KD), seed=400 + KD + H)
+    x = qkv.to(dev)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out, vres, lse = psa.psa_attention_fwd(x, h, KD, workspace=ws)
+    _check_psa_heads(qkv, B, h, KD, H, W, out, vres, lse, np.array([0, B * h - 2, B * h - 1]))
+    o_none, _, l_none = psa.psa_attention_fwd(x, h, KD)
+    assert (o_none.float() - out.float()).abs().max().item() <= 2.0 ** -7 * max(1.0, out.float().abs().max().item())
+    assert (l_none - lse).abs().max().item() < 1e-3
+
+
+@pytest.mark.parametrize("shape", [(2, 640, 640, 32), (1, 100, 1500, 64), (2, 300, 260, 128), (2, 200, 330, 16)],
+                         ids=lambda s: "BH{}_q{}_k{}_d{}".format(*s))
+def test_ramp_fa2_fwd_bwd(shape):
+    dev = device()
+    BH, nq, nk, D = shape
+    announce(f"ramp fa2_fwd/fa2_bwd BH{BH} q{nq} k{nk} d{D}")
+    q, k, v, do = I.make_ramp_attention_inputs(BH, nq, nk, D, score_step=_step(D), seed=500 + nq + D,
+                                               with_dout=True)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = psa.fa2_fwd(qd, kd, vd)
+    s = D ** -0.5
+    want_o, want_lse = O.attention(to_f64(q), to_f64(k), to_f64(v), s)
+    assert_attention_close(to_f64(o), want_o, "bf16", "ramp fa2_fwd O")
+    assert_lse_close(to_f64(lse), want_lse, "bf16", "ramp fa2_fwd")
+    grads = psa.fa2_bwd(qd, kd, vd, o, dod, lse)
+    want = O.attention_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), s)
+    for name, got, w in zip(("dQ", "dK", "dV"), grads, want):
+        assert_attention_close(to_f64(got), w, "bf16", f"ramp fa2_bwd {name}")
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 32, 16, 20), (1, 1, 64, 12, 12)], ids=_psa_id)
+def test_ramp_psa_bwd(shape):
+    dev = device()
+    B, h, KD, H, W = shape
+    announce(f"ramp psa_attention_bwd {_psa_id(shape)}")
+    qkv = I.make_ramp_qkv(B, h, KD, H, W, score_step=_step(KD), seed=600 + KD + H * W)
+    rng = np.random.default_rng(601 + KD)
+    # gradients N(0, 0.25^2): the rising queries all weight the last keys, so dK and dV sum many rows
+    dout = torch.from_numpy(0.25 * rng.standard_normal((B, 2 * h * KD, H, W)).astype(np.float32)).to(torch.bfloat16)
+    dv = torch.from_numpy(0.25 * rng.standard_normal((B, 2 * h * KD, H, W)).astype(np.float32)).to(torch.bfloat16)
+    x = qkv.to(dev)
+    out, _, lse = psa.psa_attention_fwd(x, h, KD, want_v=False)
+    got = to_f64(psa.psa_attention_bwd(x, out, lse, dout.to(dev), h, KD, dv=dv.to(dev)))
+    want = O.psa_backward(to_f64(qkv), to_f64(dout), to_f64(dv), B, h, KD, H, W)
+    g = got.reshape(B, h, 4, KD, H * W)
+    wr = want.reshape(B, h, 4, KD, H * W)
+    for s, name in enumerate(("dQ", "dK", "dV_lo", "dV_hi")):
+        assert_attention_close(g[:, :, s], wr[:, :, s], "bf16", f"ramp psa_attention_bwd {name}")
