@@ -212,3 +212,27 @@ def test_fa2_fwd_tail_split(shape):
     want_o, want_lse = O.attention(to_f64(q)[sel], to_f64(k)[sel], to_f64(v)[sel], D ** -0.5)
     assert_attention_close(to_f64(o)[sel], want_o, "bf16", "fa2_fwd tail O")
     assert_lse_close(to_f64(lse)[sel], want_lse, "bf16", "fa2_fwd tail")
+
+
+@pytest.mark.parametrize("shape", [(32, 6400, 4096, 64), (48, 2112, 3000, 64)],
+                         ids=lambda s: "BH{}q{}k{}d{}".format(*s))
+def test_fa2_fwd_tail_split_cross_lengths(shape):
+    """The tail split with n_q != n_k: pieces cut the key range of n_k keys while the split
+    tiles are counted over n_q queries; checked on the last two batch-heads and against the
+    same launch run unsplit."""
+    dev = device()
+    BH, nq, nk, D = shape
+    announce(f"fa2_fwd tail split BH{BH} q{nq} k{nk} d{D}")
+    nbytes = psa.fa2_fwd_workspace_bytes(BH, nq, nk, D)
+    assert nbytes > 0, "this grid is expected to split its last round on a 256-CU gfx950"
+    q, k, v = I.make_attention_inputs(BH, nq, nk, D, seed=37)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    o, lse = psa.fa2_fwd(qd, kd, vd, workspace=ws)
+    sel = [BH - 2, BH - 1]
+    want_o, want_lse = O.attention(to_f64(q)[sel], to_f64(k)[sel], to_f64(v)[sel], D ** -0.5)
+    assert_attention_close(to_f64(o)[sel], want_o, "bf16", "fa2_fwd tail O (n_q != n_k)")
+    assert_lse_close(to_f64(lse)[sel], want_lse, "bf16", "fa2_fwd tail (n_q != n_k)")
+    o_none, l_none = psa.fa2_fwd(qd, kd, vd, workspace=torch.empty(0, dtype=torch.uint8, device=dev))
+    assert (o_none.float() - o.float()).abs().max().item() <= 2.0 ** -7 * max(1.0, o.float().abs().max().item())
+    assert (l_none - lse).abs().max().item() < 1e-3
