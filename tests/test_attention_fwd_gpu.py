@@ -236,3 +236,36 @@ def test_fa2_fwd_tail_split_cross_lengths(shape):
     o_none, l_none = psa.fa2_fwd(qd, kd, vd, workspace=torch.empty(0, dtype=torch.uint8, device=dev))
     assert (o_none.float() - o.float()).abs().max().item() <= 2.0 ** -7 * max(1.0, o.float().abs().max().item())
     assert (l_none - lse).abs().max().item() < 1e-3
+
+
+@pytest.mark.parametrize("hw", [(1448, 1448), (1449, 1449)], ids=lambda s: "{}x{}".format(*s))
+def test_psa_fused_fwd_largest_slab(hw):
+    """The fused forward at the edge of its 32-bit buffer offsets: a key_dim-128 map whose
+    batch-head slab of Q, K, V_lo, V_hi is just under 2 GB (1448x1448: staged straight into
+    LDS with buffer loads) and just over it (1449x1449, N not a multiple of 8 either: staged
+    through registers with 64-bit addresses). 16 sampled pixels against the oracle (both
+    halves and the LSE, all 2.1 M keys); the V residual bit-exact on the whole map."""
+    dev = device()
+    H, W = hw
+    B, h, KD = 1, 1, 128
+    N = H * W
+    announce(f"psa_attention_fwd largest slab {H}x{W} key_dim {KD}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    qkv = torch.randn((B, 4 * h * KD, H, W), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out, vres, lse = psa.psa_attention_fwd(qkv, h, KD)
+    torch.cuda.synchronize()
+    assert torch.equal(vres, qkv[:, 2 * KD:4 * KD]), "V residual differs"
+    rows = np.linspace(0, N - 1, 16).astype(np.int64)
+    x = qkv.reshape(4, KD, N)
+    q = to_f64(x[0][:, torch.from_numpy(rows).to(dev)].t())[None]      # [1, 16, KD]
+    k = to_f64(x[1].t())[None]                                          # [1, N, KD]
+    want_lse = None
+    for j in range(2):
+        v = to_f64(x[2 + j].t())[None]
+        want_o, want_lse = O.attention(q, k, v, KD ** -0.5)
+        got = to_f64(out.reshape(2, KD, N)[j][:, torch.from_numpy(rows).to(dev)].t())[None]
+        assert_attention_close(got, want_o, "bf16", f"largest slab {H}x{W} half {j}")
+        del v
+    assert_lse_close(to_f64(lse.reshape(N)[torch.from_numpy(rows).to(dev)])[None], want_lse, "bf16",
+                     f"largest slab {H}x{W}")
