@@ -292,3 +292,32 @@ def test_fa2_bwd_noalloc_argument_errors():
     assert st == 2 and "scratch" in msg and str(16 << 20) in msg, msg
     st, msg = call(ptrs=p[:6] + [p[0]] + p[7:])
     assert st == 5 and "overlap" in msg
+
+
+def test_attention_rows_beyond_one_launch_are_rejected():
+    """The attention kernels give every 128 rows one workgroup and a launch holds fewer than
+    2^32 work-items, so BH * n (rounded up to 128) must stay below 2^31 - 2^23; larger calls
+    fail with PSA_ERR_SHAPE before anything is launched, naming the entry point."""
+    big_bh, big_n = 1 << 14, 1 << 17            # 2^31 rows
+    st, msg = _status("fa2_fwd", A, B_, C_, 0xB0000000, None, big_bh, big_n, 64, 16,
+                      ctypes.c_float(0.25), 1, None, 0, None)
+    assert st == 2 and msg.startswith("fa2_fwd") and "one launch" in msg, msg
+    st, msg = _status("fa2_fwd", A, B_, C_, 0xB0000000, None, big_bh, 64, big_n, 16,
+                      ctypes.c_float(0.25), 1, None, 0, None)   # many keys: the dK/dV grid's rows
+    assert st == 2 and "one launch" in msg, msg
+    base = [0x1000000 * (i + 1) for i in range(10)]
+    st, msg = _status("fa2_bwd", *base, big_bh, big_n, big_n, 16, ctypes.c_float(0.25), 1, None)
+    assert st == 2 and msg.startswith("fa2_bwd") and "one launch" in msg, msg
+    # B * heads = 8192 maps of 512 x 512 pixels: 2^31 rows
+    st, msg = _status("psa_attention_fwd", A, B_, None, None, 1024, 8, 16, 512, 512,
+                      ctypes.c_float(0.25), 1, None, 0, None)
+    assert st == 2 and msg.startswith("psa_attention_fwd") and "one launch" in msg, msg
+    bp = [0x1000000 * (i + 1) for i in range(7)]
+    st, msg = _status("psa_attention_bwd", *bp, 1024, 8, 16, 512, 512, ctypes.c_float(0.25), 1, None)
+    assert st == 2 and msg.startswith("psa_attention_bwd") and "one launch" in msg, msg
+    # just under the limit passes the size checks (and fails later, on the aliasing of the
+    # fake pointers, which shows the size check let it through)
+    ok_n = ((1 << 31) - (1 << 23)) // (1 << 14) - 128   # a multiple of 128 below the limit
+    st, msg = _status("fa2_fwd", A, A, A, A, None, 1 << 14, ok_n, 64, 16, ctypes.c_float(0.25), 1,
+                      None, 0, None)
+    assert st == 5, msg

@@ -111,3 +111,46 @@ def test_stale_hip_error_is_not_reported_as_a_launch_failure():
     packed = psa.psa_pack_qkv(x, h, KD)
     torch.cuda.synchronize()
     assert np.array_equal(bits(packed), O.pack_qkv(bits(qkv), B, h, KD, H, W))
+
+
+# The largest slabs: one (batch-head, slot) slab of key_dim 128 just under 2 GB (the LDS
+# kernels, whose NCHW-side buffer stores take 32-bit offsets) and exactly 2 GB (the scalar
+# kernel). (dtype, H, W)
+LARGEST = [("f32", 8, 524287), ("f32", 2048, 2048), ("bf16", 8, 1048575), ("bf16", 2048, 4096)]
+
+
+@pytest.mark.parametrize("case", LARGEST, ids=lambda c: "{}_{}x{}".format(*c))
+def test_layout_largest_slab(case):
+    """Pack, extract and merge on key_dim-128 maps whose slabs sit at the 2 GB edge, filled
+    with random bit patterns on the GPU. The ops move each pixel's channels independently, so
+    windows of 64 pixels (the first, one in the middle, the last) are checked against the
+    oracle applied to the same windows of the inputs, bit for bit."""
+    dev = device()
+    dt, H, W = case
+    B, h, KD = 1, 1, 128
+    N = H * W
+    announce(f"layout largest slab {dt} {H}x{W} key_dim {KD}")
+    ity, fty = (torch.int32, torch.float32) if dt == "f32" else (torch.int16, torch.bfloat16)
+    lo, hi = (-2 ** 31, 2 ** 31 - 1) if dt == "f32" else (-2 ** 15, 2 ** 15 - 1)
+    g = torch.Generator(device=dev)
+    g.manual_seed(777)
+    qkv = torch.randint(lo, hi, (B, 4 * h * KD, H, W), generator=g, dtype=ity, device=dev).view(fty)
+    packed = psa.psa_pack_qkv(qkv, h, KD)
+    v = psa.psa_extract_v(packed, B, h, KD, H, W)
+    del qkv
+    o2 = torch.randint(lo, hi, (2, B * h, N, KD), generator=g, dtype=ity, device=dev).view(fty)
+    merged = psa.psa_merge_attn(o2, B, h, KD, H, W)
+    torch.cuda.synchronize()
+    g.manual_seed(777)   # the same qkv bits again, for the windows
+    qkv = torch.randint(lo, hi, (B, 4 * h * KD, H, W), generator=g, dtype=ity, device=dev).view(fty)
+    w = 64
+    for n0 in (0, (N // 2) // w * w, N - w):
+        sl = slice(n0, n0 + w)
+        q_win = bits(qkv.reshape(B, 4 * h * KD, N)[:, :, sl]).reshape(B, 4 * h * KD, 1, w)
+        want_p = O.pack_qkv(q_win, B, h, KD, 1, w)
+        assert np.array_equal(bits(packed[:, :, sl, :]), want_p), f"pack differs at pixels {n0}.."
+        got_v = bits(v.reshape(B, 2 * h * KD, N)[:, :, sl]).reshape(B, 2 * h * KD, 1, w)
+        assert np.array_equal(got_v, O.extract_v(want_p, B, h, KD, 1, w)), f"extract differs at pixels {n0}.."
+        got_m = bits(merged.reshape(B, 2 * h * KD, N)[:, :, sl]).reshape(B, 2 * h * KD, 1, w)
+        want_m = O.merge_attn(bits(o2[:, :, sl, :]), B, h, KD, 1, w)
+        assert np.array_equal(got_m, want_m), f"merge differs at pixels {n0}.."

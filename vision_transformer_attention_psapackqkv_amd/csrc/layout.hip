@@ -79,10 +79,12 @@ struct Word<4> { using T = uint32_t; };
 
 // kToRows = true: NCHW [KD, N] slabs -> packed [N, KD] slabs (pack).
 // kToRows = false: packed [N, KD] slabs -> NCHW [KD, N] slabs (merge, extract).
+// Workgroup i of a launch moves tile i % tiles_per_slab of slab slab0 + i / tiles_per_slab.
 template <int kElt, int KD, bool kToRows, int kThreadsLds = threads_lds<kToRows>()>
 __global__ __launch_bounds__(kThreadsLds) void transpose_slabs_lds(const void* __restrict__ src_v,
                                                                    void* __restrict__ dst_v,
-                                                                   SlabGeom g, int tiles_per_slab) {
+                                                                   SlabGeom g, int tiles_per_slab,
+                                                                   int slab0) {
   using T = typename Word<kElt>::T;
   constexpr int VEC = 16 / kElt;                 // elements per 16-byte chunk
   constexpr int PX = tile_bytes<kToRows, KD>() / (KD * kElt);   // pixels per tile
@@ -92,8 +94,9 @@ __global__ __launch_bounds__(kThreadsLds) void transpose_slabs_lds(const void* _
   static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0 && KD * CPR == PER * kThreadsLds, "tile shape");
   __shared__ __attribute__((aligned(16))) T lds[KD * PX];
 
-  const int t = blockIdx.x / tiles_per_slab;
-  const int tile = blockIdx.x - t * tiles_per_slab;
+  const int local = blockIdx.x / tiles_per_slab;
+  const int tile = blockIdx.x - local * tiles_per_slab;
+  const int t = slab0 + local;
   const int p0 = tile * PX;
   const int np = min(PX, g.N - p0);   // pixels of this tile; a multiple of VEC
   int64_t nchw_off, rows_off;
@@ -174,26 +177,33 @@ __global__ __launch_bounds__(kThreadsLds) void transpose_slabs_lds(const void* _
   }
 }
 
-// Any N: one thread per element, consecutive threads walk the packed side.
+// Any N: one thread per element, consecutive threads walk the packed side. The grid
+// is capped (a launch holds fewer than 2^32 work-items) and strides over the
+// n_slabs * tiles_per_slab tiles of kThreads elements.
 template <typename T, bool kToRows>
 __global__ __launch_bounds__(kThreads) void transpose_slabs_scalar(const T* __restrict__ src,
                                                                    T* __restrict__ dst, SlabGeom g,
-                                                                   int tiles_per_slab) {
-  const int t = blockIdx.x / tiles_per_slab;
-  const int tile = blockIdx.x - t * tiles_per_slab;
-  const int64_t e = static_cast<int64_t>(tile) * kThreads + threadIdx.x;  // n*KD + d
-  if (e >= static_cast<int64_t>(g.N) * g.KD) return;
-  const int n = static_cast<int>(e / g.KD);
-  const int d = static_cast<int>(e - static_cast<int64_t>(n) * g.KD);
-  int64_t nchw_off, rows_off;
-  slab_offsets(g, t, nchw_off, rows_off);
-  const int64_t nchw_i = nchw_off + static_cast<int64_t>(d) * g.N + n;
-  const int64_t rows_i = rows_off + e;
-  if (kToRows)
-    dst[rows_i] = src[nchw_i];
-  else
-    dst[nchw_i] = src[rows_i];
+                                                                   int64_t tiles_per_slab, int64_t tiles) {
+  const int64_t per_slab = static_cast<int64_t>(g.N) * g.KD;
+  for (int64_t i = blockIdx.x; i < tiles; i += gridDim.x) {
+    const int t = static_cast<int>(i / tiles_per_slab);
+    const int64_t e = (i - t * tiles_per_slab) * kThreads + threadIdx.x;  // n*KD + d
+    if (e >= per_slab) continue;
+    const int n = static_cast<int>(e / g.KD);
+    const int d = static_cast<int>(e - static_cast<int64_t>(n) * g.KD);
+    int64_t nchw_off, rows_off;
+    slab_offsets(g, t, nchw_off, rows_off);
+    const int64_t nchw_i = nchw_off + static_cast<int64_t>(d) * g.N + n;
+    const int64_t rows_i = rows_off + e;
+    if (kToRows)
+      dst[rows_i] = src[nchw_i];
+    else
+      dst[nchw_i] = src[rows_i];
+  }
 }
+
+// Workgroups per launch: a launch holds fewer than 2^32 work-items; 2^31 keeps a margin.
+constexpr int64_t kMaxLaunchItems = int64_t(1) << 31;
 
 template <int kElt, bool kToRows>
 void launch_lds(const void* src, void* dst, SlabGeom g, int n_slabs, hipStream_t stream) {
@@ -201,8 +211,15 @@ void launch_lds(const void* src, void* dst, SlabGeom g, int n_slabs, hipStream_t
     constexpr int KD = decltype(kd)::value;
     constexpr int PX = tile_bytes<kToRows, KD>() / (KD * kElt);
     const int tiles = (g.N + PX - 1) / PX;
-    const dim3 grid(static_cast<unsigned>(n_slabs) * tiles);
-    transpose_slabs_lds<kElt, KD, kToRows><<<grid, threads_lds<kToRows>(), 0, stream>>>(src, dst, g, tiles);
+    // Whole slabs per launch, as many as one launch holds: pack takes a single launch up to
+    // 128 GB of slabs, merge and extract up to 32 GB, larger calls several.
+    const int64_t per_launch = kMaxLaunchItems / (static_cast<int64_t>(tiles) * threads_lds<kToRows>());
+    for (int64_t s0 = 0; s0 < n_slabs; s0 += per_launch) {
+      const int64_t n = n_slabs - s0 < per_launch ? n_slabs - s0 : per_launch;
+      const dim3 grid(static_cast<unsigned>(n * tiles));
+      transpose_slabs_lds<kElt, KD, kToRows><<<grid, threads_lds<kToRows>(), 0, stream>>>(
+          src, dst, g, tiles, static_cast<int>(s0));
+    }
   };
   switch (g.KD) {
     case 16: go(std::integral_constant<int, 16>{}); break;
@@ -227,14 +244,16 @@ hipError_t launch_transpose(const void* src, void* dst, SlabGeom g, int elt_byte
       launch_lds<4, kToRows>(src, dst, g, n_slabs, stream);
   } else {
     const int64_t per_slab = static_cast<int64_t>(g.N) * g.KD;
-    const int tiles = static_cast<int>((per_slab + kThreads - 1) / kThreads);
-    const dim3 grid(static_cast<unsigned>(n_slabs) * tiles);
+    const int64_t tiles_per_slab = (per_slab + kThreads - 1) / kThreads;
+    const int64_t tiles = tiles_per_slab * n_slabs;
+    const int64_t cap = kMaxLaunchItems / kThreads;
+    const dim3 grid(static_cast<unsigned>(tiles < cap ? tiles : cap));
     if (elt_bytes == 2)
       transpose_slabs_scalar<uint16_t, kToRows><<<grid, kThreads, 0, stream>>>(
-          static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), g, tiles);
+          static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), g, tiles_per_slab, tiles);
     else
       transpose_slabs_scalar<uint32_t, kToRows><<<grid, kThreads, 0, stream>>>(
-          static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), g, tiles);
+          static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), g, tiles_per_slab, tiles);
   }
   return hipGetLastError();
 }

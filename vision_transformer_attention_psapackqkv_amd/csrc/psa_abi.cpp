@@ -126,6 +126,17 @@ psa_status check_map(const char* fn, int B, int heads, int key_dim, int H, int W
   return PSA_OK;
 }
 
+// The attention kernels give each 128 rows (queries, or keys for dK/dV) one
+// workgroup of up to 256 work-items, and a launch holds fewer than 2^32
+// work-items: BH * n rounded up to 128 rows stays below 2^31 - 2^23.
+psa_status check_launch_rows(const char* fn, int64_t BH, int64_t n) {
+  const int64_t rows = BH * ((n + 127) / 128) * 128;
+  if (rows >= (int64_t(1) << 31) - (int64_t(1) << 23))
+    return fail(PSA_ERR_SHAPE, fn, "BH=%lld times %lld rows is too many for one launch (at most 2^31 - 2^23)",
+                static_cast<long long>(BH), static_cast<long long>(n));
+  return PSA_OK;
+}
+
 psa_status check_attn(const char* fn, int BH, int n_q, int n_k, int head_dim, float scale,
                       psa_dtype dtype) {
   if (BH <= 0 || n_q <= 0 || n_k <= 0 || head_dim <= 0)
@@ -139,7 +150,7 @@ psa_status check_attn(const char* fn, int BH, int n_q, int n_k, int head_dim, fl
   const int64_t rows = static_cast<int64_t>(BH) * (n_q > n_k ? n_q : n_k);
   if (n_q > (1 << 28) || n_k > (1 << 28) || rows * head_dim > (int64_t(1) << 40))
     return fail(PSA_ERR_SHAPE, fn, "sizes too large (BH=%d n_q=%d n_k=%d)", BH, n_q, n_k);
-  return PSA_OK;
+  return check_launch_rows(fn, BH, n_q > n_k ? n_q : n_k);
 }
 
 #define PSA_TRY(expr)                       \
@@ -323,6 +334,7 @@ psa_status psa_attention_fwd(const void* qkv_nchw, void* out_nchw, void* v_nchw,
   if (!qkv_nchw) return fail(PSA_ERR_NULL, fn, "qkv_nchw is NULL");
   if (!out_nchw) return fail(PSA_ERR_NULL, fn, "out_nchw is NULL");
   PSA_TRY(check_map(fn, B, heads, key_dim, H, W, dtype));
+  PSA_TRY(check_launch_rows(fn, static_cast<int64_t>(B) * heads, static_cast<int64_t>(H) * W));
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(PSA_ERR_UNSUPPORTED, fn, "scale=%g must be finite and > 0", static_cast<double>(scale));
   PSA_TRY(check_aligned(fn, "qkv_nchw", qkv_nchw));
@@ -359,6 +371,7 @@ psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const f
     return fail(PSA_ERR_NULL, fn, "qkv_nchw, out_nchw, lse, dout_nchw, dqkv_nchw and workspace "
                                   "must not be NULL (dv_nchw may be)");
   PSA_TRY(check_map(fn, B, heads, key_dim, H, W, dtype));
+  PSA_TRY(check_launch_rows(fn, static_cast<int64_t>(B) * heads, static_cast<int64_t>(H) * W));
   if (dtype != PSA_BF16)
     return fail(PSA_ERR_UNSUPPORTED, fn, "dtype=%d: only PSA_BF16 (1) is built for the backward",
                 static_cast<int>(dtype));
