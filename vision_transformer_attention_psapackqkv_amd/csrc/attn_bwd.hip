@@ -9,8 +9,9 @@
 // looping over key tiles), which also computes Delta for its query rows from
 // the O and dO rows it loads and stores it negated (the dP accumulators start
 // from -Delta) beside LSE * log2(e), then dK/dV (one workgroup per key tile,
-// looping over query tiles), which reads both. Head dim 16 runs a separate
-// Delta pass first. Neither kernel uses atomics.
+// looping over query tiles), which reads both. Head dim 16, batch-heads of
+// 2 GB or more and the float32 path run a separate Delta pass first. No kernel
+// uses atomics.
 //
 // The matrix-core products use v_mfma_f32_32x32x16_bf16 with the operand
 // placement of the forward kernel: the rows of the first products' LDS
@@ -20,11 +21,10 @@
 // rows, are read from the same row tiles with transposed LDS reads
 // (ds_read_b64_tr_b16). Head dims 32..128 stage their tiles straight from
 // global memory into swizzled unpadded rows; head dim 16 through registers
-// into padded rows.
+// into padded rows. The float32 path is one thread per row on the VALU.
 #include <math.h>
 
 #include <mutex>
-
 #include <type_traits>
 
 #include "psa_device.hpp"
