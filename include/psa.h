@@ -22,7 +22,9 @@
  *    per-process cache of device properties (CU count of each device, the
  *    occupancy of each kernel) that launches are sized with.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
- *    work is enqueued asynchronously on it.
+ *    work is enqueued asynchronously on it. The stream and every buffer belong
+ *    to the calling thread's current HIP device (hipSetDevice): launch sizes
+ *    and fa2_bwd_noalloc's scratch are taken for that device.
  *  - Outputs are overwritten, never accumulated into. Inputs are read only.
  *  - Every argument is validated before anything is launched. On any error
  *    nothing is enqueued, nothing is written, the status says which class of

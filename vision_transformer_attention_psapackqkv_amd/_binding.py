@@ -8,6 +8,7 @@ a call fails, an exception is raised.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -74,6 +75,19 @@ def _check(status: int):
         raise PsaError(status, load_library().psa_last_error().decode())
 
 
+def _on_device(fn):
+    """Runs a binding entry point with its first tensor argument's GPU as the current HIP
+    device: the library sizes launches (and picks fa2_bwd_noalloc's scratch) for the current
+    device, and the tensors and stream passed are that GPU's."""
+    @functools.wraps(fn)
+    def wrapper(t, *args, **kwargs):
+        if isinstance(t, torch.Tensor) and t.device.type == "cuda" and t.device.index != torch.cuda.current_device():
+            with torch.cuda.device(t.device):
+                return fn(t, *args, **kwargs)
+        return fn(t, *args, **kwargs)
+    return wrapper
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return PSA_BF16
@@ -138,6 +152,7 @@ def default_scale(key_dim: int) -> float:
     return float(key_dim) ** -0.5
 
 
+@_on_device
 def psa_pack_qkv(qkv: torch.Tensor, heads: int, key_dim: int, out: torch.Tensor | None = None):
     """qkv NCHW ``[B, 4*heads*key_dim, H, W]`` -> packed ``[4, B*heads, H*W, key_dim]``."""
     B, H, W = _nchw(qkv, heads, key_dim)
@@ -164,11 +179,13 @@ def _rows_to_nchw(fn_name, rows, slots, B, heads, key_dim, H, W, out):
     return out
 
 
+@_on_device
 def psa_extract_v(packed, B, heads, key_dim, H, W, out=None):
     """packed ``[4, B*heads, H*W, key_dim]`` -> V residual NCHW ``[B, 2*heads*key_dim, H, W]``."""
     return _rows_to_nchw("psa_extract_v", packed, 4, B, heads, key_dim, H, W, out)
 
 
+@_on_device
 def psa_merge_attn(o2, B, heads, key_dim, H, W, out=None):
     """o2 ``[2, B*heads, H*W, key_dim]`` -> NCHW ``[B, 2*heads*key_dim, H, W]``."""
     return _rows_to_nchw("psa_merge_attn", o2, 2, B, heads, key_dim, H, W, out)
@@ -212,6 +229,7 @@ def _qkv3(q, k, v):
     return BH, n_q, D, n_k
 
 
+@_on_device
 def fa2_fwd(q, k, v, scale=None, out=None, lse=None, want_lse=True, workspace=None):
     """FA2 forward on ``[BH, n, D]`` tensors; returns ``(o, lse)`` (lse is None if not wanted).
 
@@ -234,6 +252,7 @@ def fa2_fwd(q, k, v, scale=None, out=None, lse=None, want_lse=True, workspace=No
     return out, lse
 
 
+@_on_device
 def fa2_bwd(q, k, v, o, dout, lse, scale=None, workspace=None):
     """FA2 backward; returns ``(dq, dk, dv)``.
 
@@ -260,6 +279,7 @@ def fa2_bwd(q, k, v, o, dout, lse, scale=None, workspace=None):
 NOALLOC_SCRATCH_BYTES = 16 << 20   # PSA_NOALLOC_SCRATCH_BYTES of include/psa.h
 
 
+@_on_device
 def fa2_bwd_noalloc(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None):
     """FA2 backward through ``fa2_bwd_noalloc``: no workspace, the library keeps -Delta in its
     own device scratch (BH * n_q <= NOALLOC_SCRATCH_BYTES / 8). Returns ``(dq, dk, dv)``; pass
@@ -282,6 +302,7 @@ def fa2_bwd_noalloc(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None
     return dq, dk, dv
 
 
+@_on_device
 def psa_attention_fwd(qkv, heads, key_dim, scale=None, want_v=True, want_lse=True,
                       out=None, v_out=None, lse=None, workspace=None):
     """Fused PSA forward on NCHW ``qkv``; returns ``(out, v_residual, lse)`` (None where not wanted).
@@ -311,6 +332,7 @@ def psa_attention_fwd(qkv, heads, key_dim, scale=None, want_v=True, want_lse=Tru
     return out, v_out, lse
 
 
+@_on_device
 def psa_attention_bwd(qkv, out, lse, dout, heads, key_dim, dv=None, scale=None, dqkv=None,
                       workspace=None):
     """PSA backward: the gradient of ``psa_attention_fwd``'s outputs with respect to ``qkv``.
@@ -380,6 +402,7 @@ def _f32(t, name, shape=None):
     return t
 
 
+@_on_device
 def detect_decode(boxes, anchor_x, anchor_y, strides, out=None):
     """LTRB ``boxes [B, 4, A]`` (float32 or bf16) + anchor grid ``[A]`` x3 (float32) ->
     ``[B, 4, A]`` cx, cy, w, h in the dtype of ``boxes``."""
@@ -399,6 +422,7 @@ def detect_decode(boxes, anchor_x, anchor_y, strides, out=None):
     return out
 
 
+@_on_device
 def ciou_loss_fwd(pred, target, out=None):
     """``pred, target [4, N]`` float32 cx, cy, w, h -> ``(loss, iou, v, alpha)``, each ``[N]``
     (written into ``out``, a tuple of four such tensors, if given)."""
@@ -416,6 +440,7 @@ def ciou_loss_fwd(pred, target, out=None):
     return loss, iou, v, alpha
 
 
+@_on_device
 def ciou_loss_bwd(pred, target, iou, v, alpha, dloss, dpred=None):
     """Gradient ``[4, N]`` of ``sum(dloss * loss)`` w.r.t. ``pred`` from the forward's saved
     ``iou, v, alpha`` (alpha held constant)."""
