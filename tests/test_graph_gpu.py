@@ -108,3 +108,47 @@ def test_detect_decode_and_ciou_in_a_graph():
         launches()
     y = torch.randn(1 << 20, device=dev)
     _replays_match(g, list(dec.values()) + list(fwd) + [dp], eager, lambda: y.mul_(1.5))
+
+
+def test_fa2_and_layout_in_a_graph():
+    """The unfused chain's calls (pack, fa2_fwd on both V halves with the tail-split
+    workspace, merge, extract) and the FA2 backward through fa2_bwd_noalloc, the entry point
+    meant for capture (it allocates nothing: its -Delta rows live in the library's scratch),
+    in one captured graph."""
+    dev = device()
+    B, h, KD, H, W = 2, 8, 64, 80, 80     # the FA2 grid splits its last round
+    announce("pack + fa2_fwd x2 + merge + extract + fa2_bwd_noalloc graph capture")
+    x = I.make_qkv(B, h, KD, H, W, seed=45).to(dev)
+    BH, N = B * h, H * W
+    packed = torch.empty((4, BH, N, KD), dtype=x.dtype, device=dev)
+    o2 = torch.empty((2, BH, N, KD), dtype=x.dtype, device=dev)
+    lse = torch.empty((BH, N), dtype=torch.float32, device=dev)
+    merged = torch.empty((B, 2 * h * KD, H, W), dtype=x.dtype, device=dev)
+    vres = torch.empty_like(merged)
+    ws = torch.empty(psa.fa2_fwd_workspace_bytes(BH, N, N, KD), dtype=torch.uint8, device=dev)
+    assert ws.numel() > 0
+    dout = torch.randn((BH, N, KD), device=dev).to(x.dtype)
+    grads = [torch.empty((BH, N, KD), dtype=x.dtype, device=dev) for _ in range(3)]
+
+    def launches():
+        psa.psa_pack_qkv(x, h, KD, out=packed)
+        psa.fa2_fwd(packed[0], packed[1], packed[2], out=o2[0], lse=lse, workspace=ws)
+        psa.fa2_fwd(packed[0], packed[1], packed[3], out=o2[1], want_lse=False, workspace=ws)
+        psa.psa_merge_attn(o2, B, h, KD, H, W, out=merged)
+        psa.psa_extract_v(packed, B, h, KD, H, W, out=vres)
+        psa.fa2_bwd_noalloc(packed[0], packed[1], packed[2], o2[0], dout, lse,
+                            dq=grads[0], dk=grads[1], dv=grads[2])
+    launches()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in [packed, o2, lse, merged, vres] + grads]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launches()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launches()
+    y = torch.randn(1 << 20, device=dev)
+    _replays_match(g, [packed, o2, lse, merged, vres] + grads, eager, lambda: y.mul_(1.5))
