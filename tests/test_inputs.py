@@ -37,3 +37,25 @@ def test_bwd_inputs_and_views():
     bits = I.raw_bits(q)
     assert bits.dtype == np.uint16
     assert np.array_equal(I.as_f64(q), q.to(torch.float64).numpy())
+
+
+def test_score_ramp_inputs():
+    """The ramp generators: deterministic; even queries' dot products climb by score_step per
+    key and odd queries' fall, up to the small noise; the NCHW form puts the same kind of rows
+    in the query and key channels and leaves V N(0, 1)."""
+    step = 0.75
+    q, k, v, do = I.make_ramp_attention_inputs(2, 6, 300, 32, score_step=step, seed=9, with_dout=True)
+    q2 = I.make_ramp_attention_inputs(2, 6, 300, 32, score_step=step, seed=9)[0]
+    assert torch.equal(q, q2) and q.dtype == torch.bfloat16 and do.shape == (2, 6, 32)
+    s = torch.einsum("bnd,bmd->bnm", q.double(), k.double())
+    m = torch.arange(300, dtype=torch.float64)
+    assert (s[:, 0::2] - m * step).abs().max() < 3.0 + 0.02 * 300 * step    # noise plus bf16 rounding
+    assert (s[:, 1::2] + m * step).abs().max() < 3.0 + 0.02 * 300 * step
+    assert float(do.float().std()) < 0.5                                    # dO ~ N(0, 0.25^2)
+    x = I.make_ramp_qkv(1, 2, 16, 5, 6, score_step=step, seed=4)
+    g = x.reshape(1, 2, 4, 16, 30).double()
+    sc = torch.einsum("bhdn,bhdm->bhnm", g[:, :, 0], g[:, :, 1])           # q_n . k_m per head
+    n30 = torch.arange(30, dtype=torch.float64)
+    assert (sc[:, :, 0::2] - n30 * step).abs().max() < 3.0
+    assert (sc[:, :, 1::2] + n30 * step).abs().max() < 3.0
+    assert abs(float(g[:, :, 2:].std()) - 1.0) < 0.2
