@@ -269,3 +269,33 @@ def test_psa_fused_fwd_largest_slab(hw):
         del v
     assert_lse_close(to_f64(lse.reshape(N)[torch.from_numpy(rows).to(dev)])[None], want_lse, "bf16",
                      f"largest slab {H}x{W}")
+
+
+@pytest.mark.parametrize("kd", [16, 32, 64, 128])
+def test_psa_fused_fwd_degenerate_scores(kd):
+    """Degenerate score rows: with the query channels zero every score is 0, so each output
+    row is the mean of the V rows over all N keys and LSE = ln N (a closed form, and the oracle
+    agrees); with every key row identical the same holds whatever the queries. Ties everywhere:
+    the running max is set once and never moves."""
+    dev = device()
+    B, h, H, W = 2, 2, 13, 17
+    N = H * W
+    announce(f"psa_attention_fwd degenerate scores kd{kd}")
+    qkv = I.make_qkv(B, h, kd, H, W, seed=60 + kd)
+    g = qkv.clone().reshape(B, h, 4, kd, N)
+    g[:, :, 0] = 0                                            # Q = 0
+    zq = g.reshape(qkv.shape).contiguous()
+    g = qkv.clone().reshape(B, h, 4, kd, N)
+    g[:, :, 1] = g[:, :, 1, :, :1]                            # every key row equals the first
+    same_k = g.reshape(qkv.shape).contiguous()
+    for name, x in (("Q = 0", zq), ("identical keys", same_k)):
+        out, _, lse = psa.psa_attention_fwd(x.to(dev), h, kd)
+        v = to_f64(x).reshape(B * h, 4, kd, N)[:, 2:]          # [BH, 2, KD, N]
+        want = np.broadcast_to(v.mean(axis=-1, keepdims=True), v.shape).reshape(B * h, 2 * kd, N)
+        got = to_f64(out).reshape(B * h, 2 * kd, N)
+        assert_attention_close(got, want, "bf16", f"{name}: out vs mean of V")
+        if name == "Q = 0":
+            assert np.abs(to_f64(lse) - np.log(N)).max() < 5e-3, "LSE is not ln N"
+        want_out, _, want_lse = O.psa_forward(to_f64(x), B, h, kd, H, W)
+        assert_attention_close(to_f64(out), want_out, "bf16", f"{name}: out vs oracle")
+        assert_lse_close(to_f64(lse), want_lse, "bf16", f"{name}")
