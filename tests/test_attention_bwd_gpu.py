@@ -88,3 +88,19 @@ def test_fa2_bwd_workload_40x40():
     # |sum_n dO| is ~40 here; bf16 rounding of P and of each dV element (<= 2^-9 relative)
     # keeps the difference near 1e-2
     assert np.abs(dv_sum - do_sum).max() < 0.1, np.abs(dv_sum - do_sum).max()
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+def test_fa2_bwd_zero_queries(D):
+    """Q = 0: every P row is uniform (1/n_k), so dV[m] = (1/n_k) * sum_n dO[n] for every key m
+    and dK = scale * dS^T Q = 0 exactly; dQ against the oracle."""
+    dev = device()
+    BH, nq, nk = 3, 150, 200
+    announce(f"fa2_bwd zero queries d{D}")
+    q, k, v, do = I.make_attention_inputs(BH, nq, nk, D, seed=70 + D, with_dout=True)
+    q = torch.zeros_like(q)
+    dq, dk, dv = _run_bwd(q, k, v, do, dev)
+    want_dv = np.broadcast_to(to_f64(do).sum(axis=1, keepdims=True) / nk, (BH, nk, D))
+    assert_attention_close(to_f64(dv), want_dv, "bf16", "dV vs (1/n_k) sum dO")
+    assert float(dk.float().abs().max()) == 0.0, "dK is not zero"
+    _check((dq, dk, dv), q, k, v, do, "bf16")
