@@ -145,3 +145,25 @@ def test_autograd_wrapper(with_v_grad):
     assert torch.equal(x.grad, dx_ref)
     want = O.psa_backward(to_f64(qkv), to_f64(dout), to_f64(dv) if with_v_grad else None, B, h, KD, H, W)
     assert_attention_close(to_f64(x.grad), want, "bf16", "d(qkv) via autograd")
+
+
+@pytest.mark.parametrize("kd", [16, 32, 64, 128])
+def test_psa_attention_bwd_zero_queries(kd):
+    """Query channels zero: P is uniform over the N pixels, so the K channels' gradient is
+    exactly 0 and each V half's gradient is (1/N) * sum over pixels of that half's dOut, plus
+    the V-residual gradient; the Q channels against the oracle."""
+    dev = device()
+    B, h, H, W = 2, 2, 12, 11
+    N = H * W
+    announce(f"psa_attention_bwd zero queries kd{kd}")
+    qkv, dout, dv = _inputs(B, h, kd, H, W, 80 + kd, True)
+    g = qkv.clone().reshape(B, h, 4, kd, N)
+    g[:, :, 0] = 0
+    qkv = g.reshape(qkv.shape).contiguous()
+    got = to_f64(_run(qkv, dout, dv, h, kd, dev)).reshape(B, h, 4, kd, N)
+    assert np.abs(got[:, :, 1]).max() == 0.0, "dK is not zero"
+    do = to_f64(dout).reshape(B, h, 2, kd, N)
+    want_v = np.broadcast_to(do.sum(axis=-1, keepdims=True) / N, do.shape) + to_f64(dv).reshape(B, h, 2, kd, N)
+    assert_attention_close(got[:, :, 2:], want_v, "bf16", "dV halves vs (1/N) sum dOut + dV_res")
+    want = O.psa_backward(to_f64(qkv), to_f64(dout), to_f64(dv), B, h, kd, H, W).reshape(B, h, 4, kd, N)
+    assert_attention_close(got[:, :, 0], want[:, :, 0], "bf16", "dQ vs oracle")
