@@ -216,8 +216,9 @@ size_t psa_attention_fwd_workspace_bytes(int B, int heads, int key_dim, int H, i
  * dout_nchw: [B, 2*h*KD, H, W] gradient of out. dv_nchw: [B, 2*h*KD, H, W]
  * gradient of the V residual, or NULL for none. dqkv_nchw: [B, 4*h*KD, H, W]
  * output. workspace: caller-owned float32 scratch of
- * psa_attention_bwd_workspace_bytes(B, heads, H, W) bytes. PSA_BF16 only
- * (PSA_F32 returns PSA_ERR_UNSUPPORTED). scale: the forward's.
+ * psa_attention_bwd_workspace_bytes(B, heads, H, W) bytes. PSA_BF16 (matrix
+ * cores, one backward for both halves) or PSA_F32 (float32 on the VALU, one V
+ * half after the other). scale: the forward's.
  */
 psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const float* lse,
                              const void* dout_nchw, const void* dv_nchw, void* dqkv_nchw,

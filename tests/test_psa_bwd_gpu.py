@@ -167,3 +167,47 @@ def test_psa_attention_bwd_zero_queries(kd):
     assert_attention_close(got[:, :, 2:], want_v, "bf16", "dV halves vs (1/N) sum dOut + dV_res")
     want = O.psa_backward(to_f64(qkv), to_f64(dout), to_f64(dv), B, h, kd, H, W).reshape(B, h, 4, kd, N)
     assert_attention_close(got[:, :, 0], want[:, :, 0], "bf16", "dQ vs oracle")
+
+
+# float32 (PSA_F32): the VALU path, one V half after the other. Every key_dim, N a multiple of
+# 8 or not, with and without the V-residual gradient; float32 tolerance against the oracle.
+F32_SHAPES = [(1, 2, 16, 8, 8), (2, 1, 32, 7, 9), (1, 2, 64, 10, 13), (1, 1, 128, 9, 12), (1, 1, 16, 1, 1)]
+
+
+@pytest.mark.parametrize("with_dv", [False, True], ids=["no_dv", "dv"])
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=_id)
+def test_psa_attention_bwd_f32(shape, with_dv):
+    dev = device()
+    B, h, KD, H, W = shape
+    announce(f"psa_attention_bwd f32 {_id(shape)} dv={with_dv}")
+    seed = 23 * B + h + KD + H * W
+    qkv = I.make_qkv(B, h, KD, H, W, dtype="f32", dist="uniform", seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    dout = torch.from_numpy(rng.standard_normal((B, 2 * h * KD, H, W)).astype(np.float32))
+    dv = torch.from_numpy(rng.standard_normal((B, 2 * h * KD, H, W)).astype(np.float32)) if with_dv else None
+    got = _run(qkv, dout, dv, h, KD, dev)
+    assert got.dtype == torch.float32
+    want = O.psa_backward(to_f64(qkv), to_f64(dout), None if dv is None else to_f64(dv), B, h, KD, H, W)
+    g = to_f64(got).reshape(B, h, 4, KD, H * W)
+    wr = want.reshape(B, h, 4, KD, H * W)
+    for s, name in enumerate(("dQ", "dK", "dV_lo", "dV_hi")):
+        assert_attention_close(g[:, :, s], wr[:, :, s], "f32", f"psa_attention_bwd f32 {name}")
+
+
+def test_psa_attention_autograd_f32():
+    """The autograd op in float32: forward and d(qkv) through the float32 kernels match the
+    oracle's forward and backward."""
+    dev = device()
+    B, h, KD, H, W = 1, 2, 32, 6, 7
+    announce("psa_attention autograd f32")
+    qkv = I.make_qkv(B, h, KD, H, W, dtype="f32", dist="uniform", seed=123)
+    x = qkv.to(dev).requires_grad_()
+    out, vres = psa.psa_attention(x, h, KD)
+    rng = np.random.default_rng(124)
+    g_out = torch.from_numpy(rng.standard_normal(tuple(out.shape)).astype(np.float32)).to(dev)
+    g_v = torch.from_numpy(rng.standard_normal(tuple(out.shape)).astype(np.float32)).to(dev)
+    torch.autograd.backward([out, vres], [g_out, g_v])
+    want_out, _, _ = O.psa_forward(to_f64(qkv), B, h, KD, H, W)
+    assert_attention_close(to_f64(out), want_out, "f32", "autograd f32 out")
+    want = O.psa_backward(to_f64(qkv), to_f64(g_out), to_f64(g_v), B, h, KD, H, W)
+    assert_attention_close(to_f64(x.grad), want, "f32", "autograd f32 d(qkv)")

@@ -389,7 +389,7 @@ def psa_attention(qkv, heads, key_dim, scale=None, workspace=None):
     """The PSA attention block as a differentiable op: NCHW ``qkv`` -> ``(out, v_residual)``.
 
     Forward is ``psa_attention_fwd``; the gradient with respect to ``qkv`` (from both outputs)
-    is ``psa_attention_bwd``. bf16 only for the backward (the library's PSA backward)."""
+    is ``psa_attention_bwd``; bf16 or float32."""
     return _PsaAttention.apply(qkv, heads, key_dim, scale, workspace)
 
 

@@ -34,6 +34,12 @@
 // (tile_chunk_pos), read both ways; they are filled straight from global memory
 // (buffer loads with an LDS destination) when N is a multiple of 8, through registers
 // otherwise. Scores use base 2: P = 2^(S * s*log2(e) - LSE*log2(e)).
+//
+// float32 (PSA_F32): one thread per row on the VALU, in float32 with expf, one
+// V half at a time. Delta, dS, dQ and dK are linear over the halves (Delta =
+// Delta_lo + Delta_hi, dS = dS_lo + dS_hi with dS_j = P * (dO_j V_j^T -
+// Delta_j)), so each half runs a Delta pass, a dK/dV pass and a dQ pass, and
+// the second half adds its dQ and dK to the first's.
 #include <math.h>
 
 #include <type_traits>
@@ -560,6 +566,168 @@ __global__ __launch_bounds__(kThreadsBwd, kOcc) void psa_bwd_dq(PsaBwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- float32
+
+struct PsaBwdF32Args {
+  const float* qkv;    // [BH * 4KD, N]
+  const float* o;      // [BH * DV, N]
+  const float* dout;   // [BH * DV, N]
+  const float* dvres;  // [BH * DV, N] or null
+  const float* lse;    // [BH, N], natural log
+  float* delta;        // [BH, N]: -Delta_j of the current half
+  float* dqkv;         // [BH * 4KD, N]
+  int BH, N, KD, j;    // j: the V half (0: lo, 1: hi)
+  float scale;
+};
+
+constexpr int kF32Threads = 128;   // one row per thread
+constexpr int kF32Rows = 32;       // rows per LDS tile
+
+// -Delta_j = -sum over half j's channels of dO * O, one thread per pixel.
+__global__ __launch_bounds__(256) void psa_bwd_delta_f32(PsaBwdF32Args a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(a.BH) * a.N) return;
+  const int bh = static_cast<int>(i / a.N);
+  const int n = static_cast<int>(i - static_cast<int64_t>(bh) * a.N);
+  const int64_t base = (static_cast<int64_t>(bh) * 2 * a.KD + a.j * a.KD) * a.N + n;
+  float s = 0.0f;
+  for (int c = 0; c < a.KD; ++c) s = fmaf(a.dout[base + static_cast<int64_t>(c) * a.N], a.o[base + static_cast<int64_t>(c) * a.N], s);
+  a.delta[i] = -s;
+}
+
+// dK (summed over the halves) and dV_j: one thread per key, queries staged through LDS.
+template <int KD>
+__global__ __launch_bounds__(kF32Threads) void psa_bwd_dkdv_f32(PsaBwdF32Args a) {
+  __shared__ float qs[kF32Rows][KD];
+  __shared__ float gs[kF32Rows][KD];
+  __shared__ float ls[kF32Rows], dls[kF32Rows];
+  const int N = a.N;
+  const int blocks = (N + kF32Threads - 1) / kF32Threads;
+  const int bh = blockIdx.x / blocks;
+  const int m = (blockIdx.x % blocks) * kF32Threads + threadIdx.x;
+  const bool ok = m < N;
+  const int mc = ok ? m : 0;
+  const float* Q = a.qkv + static_cast<int64_t>(bh) * 4 * KD * N;   // channel rows of this head
+  const float* G = a.dout + (static_cast<int64_t>(bh) * 2 + a.j) * KD * N;
+  float kr[KD], vr[KD], dk[KD], dv[KD];
+#pragma unroll
+  for (int d = 0; d < KD; ++d) {
+    kr[d] = Q[static_cast<int64_t>(KD + d) * N + mc];
+    vr[d] = Q[static_cast<int64_t>((2 + a.j) * KD + d) * N + mc];
+    dk[d] = dv[d] = 0.0f;
+  }
+  for (int q0 = 0; q0 < N; q0 += kF32Rows) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kF32Rows * KD; e += kF32Threads) {
+      const int r = e % kF32Rows, d = e / kF32Rows;
+      const bool in = q0 + r < N;
+      qs[r][d] = in ? Q[static_cast<int64_t>(d) * N + q0 + r] : 0.0f;
+      gs[r][d] = in ? G[static_cast<int64_t>(d) * N + q0 + r] : 0.0f;
+    }
+    if (threadIdx.x < kF32Rows) {
+      const int r = threadIdx.x;
+      const bool in = q0 + r < N;
+      ls[r] = in ? a.lse[static_cast<int64_t>(bh) * N + q0 + r] : 0.0f;
+      dls[r] = in ? a.delta[static_cast<int64_t>(bh) * N + q0 + r] : 0.0f;
+    }
+    __syncthreads();
+    const int cnt = min(kF32Rows, N - q0);
+    for (int r = 0; r < cnt; ++r) {
+      float sc = 0.0f, dp = 0.0f;
+#pragma unroll
+      for (int d = 0; d < KD; ++d) {
+        sc = fmaf(qs[r][d], kr[d], sc);
+        dp = fmaf(gs[r][d], vr[d], dp);
+      }
+      const float p = expf(sc * a.scale - ls[r]);
+      const float ds = p * (dp + dls[r]);   // dls holds -Delta_j
+#pragma unroll
+      for (int d = 0; d < KD; ++d) {
+        dv[d] = fmaf(p, gs[r][d], dv[d]);
+        dk[d] = fmaf(ds, qs[r][d], dk[d]);
+      }
+    }
+  }
+  if (!ok) return;
+  float* out = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N;
+  const float* res = a.dvres ? a.dvres + (static_cast<int64_t>(bh) * 2 + a.j) * KD * N : nullptr;
+#pragma unroll
+  for (int d = 0; d < KD; ++d) {
+    float* pk = out + static_cast<int64_t>(KD + d) * N + m;
+    *pk = a.j == 0 ? dk[d] * a.scale : *pk + dk[d] * a.scale;
+    out[static_cast<int64_t>((2 + a.j) * KD + d) * N + m] = res ? dv[d] + res[static_cast<int64_t>(d) * N + m] : dv[d];
+  }
+}
+
+// dQ (summed over the halves): one thread per query, keys staged through LDS.
+template <int KD>
+__global__ __launch_bounds__(kF32Threads) void psa_bwd_dq_f32(PsaBwdF32Args a) {
+  __shared__ float ks[kF32Rows][KD];
+  __shared__ float vs[kF32Rows][KD];
+  const int N = a.N;
+  const int blocks = (N + kF32Threads - 1) / kF32Threads;
+  const int bh = blockIdx.x / blocks;
+  const int n = (blockIdx.x % blocks) * kF32Threads + threadIdx.x;
+  const bool ok = n < N;
+  const int nc = ok ? n : 0;
+  const float* Q = a.qkv + static_cast<int64_t>(bh) * 4 * KD * N;
+  const float* G = a.dout + (static_cast<int64_t>(bh) * 2 + a.j) * KD * N;
+  float qr[KD], gr[KD], dq[KD];
+#pragma unroll
+  for (int d = 0; d < KD; ++d) {
+    qr[d] = Q[static_cast<int64_t>(d) * N + nc];
+    gr[d] = G[static_cast<int64_t>(d) * N + nc];
+    dq[d] = 0.0f;
+  }
+  const float lse = a.lse[static_cast<int64_t>(bh) * N + nc];
+  const float dl = a.delta[static_cast<int64_t>(bh) * N + nc];   // -Delta_j
+  for (int m0 = 0; m0 < N; m0 += kF32Rows) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kF32Rows * KD; e += kF32Threads) {
+      const int r = e % kF32Rows, d = e / kF32Rows;
+      const bool in = m0 + r < N;
+      ks[r][d] = in ? Q[static_cast<int64_t>(KD + d) * N + m0 + r] : 0.0f;
+      vs[r][d] = in ? Q[static_cast<int64_t>((2 + a.j) * KD + d) * N + m0 + r] : 0.0f;
+    }
+    __syncthreads();
+    const int cnt = min(kF32Rows, N - m0);
+    for (int r = 0; r < cnt; ++r) {
+      float sc = 0.0f, dp = 0.0f;
+#pragma unroll
+      for (int d = 0; d < KD; ++d) {
+        sc = fmaf(qr[d], ks[r][d], sc);
+        dp = fmaf(gr[d], vs[r][d], dp);
+      }
+      const float ds = expf(sc * a.scale - lse) * (dp + dl);
+#pragma unroll
+      for (int d = 0; d < KD; ++d) dq[d] = fmaf(ds, ks[r][d], dq[d]);
+    }
+  }
+  if (!ok) return;
+  float* out = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N;
+#pragma unroll
+  for (int d = 0; d < KD; ++d) {
+    float* p = out + static_cast<int64_t>(d) * N + n;
+    *p = a.j == 0 ? dq[d] * a.scale : *p + dq[d] * a.scale;
+  }
+}
+
+template <int KD>
+hipError_t run_psa_bwd_f32(PsaBwdF32Args a, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(a.BH) * a.N;
+  const dim3 grid_delta(static_cast<unsigned>((rows + 255) / 256));
+  const dim3 grid(static_cast<unsigned>(a.BH) * ((a.N + kF32Threads - 1) / kF32Threads));
+  for (int j = 0; j < 2; ++j) {   // the second half adds its dQ and dK to the first's
+    a.j = j;
+    psa_bwd_delta_f32<<<grid_delta, 256, 0, stream>>>(a);
+    psa_bwd_dkdv_f32<KD><<<grid, kF32Threads, 0, stream>>>(a);
+    psa_bwd_dq_f32<KD><<<grid, kF32Threads, 0, stream>>>(a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
 template <int KD>
 hipError_t run_psa_bwd(PsaBwdArgs a, hipStream_t stream) {
   // Workgroups per CU the registers must allow: three up to key_dim 32, two at
@@ -589,7 +757,19 @@ hipError_t run_psa_bwd(PsaBwdArgs a, hipStream_t stream) {
 
 hipError_t launch_psa_fused_bwd(const void* qkv, const void* out, const float* lse, const void* dout,
                                 const void* dvres, void* dqkv, float* workspace, int BH, int KD,
-                                int N, float scale, hipStream_t stream) {
+                                int N, float scale, bool bf16, hipStream_t stream) {
+  if (!bf16) {
+    PsaBwdF32Args f{static_cast<const float*>(qkv), static_cast<const float*>(out),
+                    static_cast<const float*>(dout), static_cast<const float*>(dvres), lse, workspace,
+                    static_cast<float*>(dqkv), BH, N, KD, 0, scale};
+    switch (KD) {
+      case 16: return run_psa_bwd_f32<16>(f, stream);
+      case 32: return run_psa_bwd_f32<32>(f, stream);
+      case 64: return run_psa_bwd_f32<64>(f, stream);
+      case 128: return run_psa_bwd_f32<128>(f, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   PsaBwdArgs a{};
   a.qkv = static_cast<const uint16_t*>(qkv);
   a.o = static_cast<const uint16_t*>(out);

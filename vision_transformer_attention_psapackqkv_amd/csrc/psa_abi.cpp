@@ -372,9 +372,6 @@ psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const f
                                   "must not be NULL (dv_nchw may be)");
   PSA_TRY(check_map(fn, B, heads, key_dim, H, W, dtype));
   PSA_TRY(check_launch_rows(fn, static_cast<int64_t>(B) * heads, static_cast<int64_t>(H) * W));
-  if (dtype != PSA_BF16)
-    return fail(PSA_ERR_UNSUPPORTED, fn, "dtype=%d: only PSA_BF16 (1) is built for the backward",
-                static_cast<int>(dtype));
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(PSA_ERR_UNSUPPORTED, fn, "scale=%g must be finite and > 0", static_cast<double>(scale));
   const char* names[7] = {"qkv_nchw", "out_nchw", "lse", "dout_nchw", "dv_nchw", "dqkv_nchw", "workspace"};
@@ -397,7 +394,8 @@ psa_status psa_attention_bwd(const void* qkv_nchw, const void* out_nchw, const f
     }
   return launched(fn, [&] {
     return psa::launch_psa_fused_bwd(qkv_nchw, out_nchw, lse, dout_nchw, dv_nchw, dqkv_nchw,
-                                     workspace, B * heads, key_dim, H * W, scale, as_stream(stream));
+                                     workspace, B * heads, key_dim, H * W, scale, dtype == PSA_BF16,
+                                     as_stream(stream));
   });
 }
 

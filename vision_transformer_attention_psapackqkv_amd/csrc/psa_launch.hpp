@@ -35,7 +35,7 @@ size_t psa_fused_split_bytes(int BH, int KD, int N, bool bf16);
 // workspace: 2 * BH * N floats (-Delta, LSE * log2(e)).
 hipError_t launch_psa_fused_bwd(const void* qkv, const void* out, const float* lse, const void* dout,
                                 const void* dvres, void* dqkv, float* workspace, int BH, int KD,
-                                int N, float scale, hipStream_t stream);
+                                int N, float scale, bool bf16, hipStream_t stream);
 
 // FA2 backward: -Delta and LSE * log2(e) into the workspace (2 * BH * n_q
 // floats), then the dK/dV and dQ kernels.
