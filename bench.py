@@ -59,6 +59,8 @@ def parse_args():
                     help="time only the PSA backward on the 40x40 map (for profiling)")
     ap.add_argument("--yolo-only", action="store_true",
                     help="time only detect-decode and the CIoU loss kernels (for profiling)")
+    ap.add_argument("--small-only", action="store_true",
+                    help="time only the 8x8 and 20x20 maps, eager and as HIP-graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy 3 times (HBM counter calibration)")
     return ap.parse_args()
@@ -252,6 +254,9 @@ def main():
     if args.yolo_only:
         print(json.dumps(yolo_components(torch, psa, dev, args.steps, args.warmup)))
         return
+    if args.small_only:
+        print(json.dumps(small_map_components(torch, psa, I, dev, args.steps, args.warmup)))
+        return
     w = I.WORKLOADS[WORKLOAD]
     qkv_cpu = I.make_workload_qkv(w)
     qkv = qkv_cpu.to(dev)
@@ -433,6 +438,7 @@ def components(torch, psa, I, w, qkv, args):
         {"avg_ms": round(avg, 5), "TFLOP/s": round(t2, 3), "pct_bf16_mfma_peak": round(100 * t2 / PEAK_BF16_TFLOPS, 2)},
         f2, steps, torch, flops2)
     del q2, o_2, v_2, l_2
+    comp.update(small_map_components(torch, psa, I, dev, steps, warm))
     comp["fa2_bwd_40x40"] = fa2_bwd_component(torch, psa, I, dev, steps, warm)
     comp["psa_bwd_40x40"] = psa_bwd_component(torch, psa, I, dev, steps, warm)
     comp.update(yolo_components(torch, psa, dev, steps, warm))
@@ -539,6 +545,44 @@ def fa2_bwd_component(torch, psa, I, dev, steps, warm):
     return with_back_to_back(
         {"avg_ms": round(avg, 5), "TFLOP/s": round(tb, 3), "pct_bf16_mfma_peak": round(100 * tb / PEAK_BF16_TFLOPS, 2),
          "flops": "10*BH*N^2*D"}, fn, steps, torch, flops)
+
+
+def small_map_components(torch, psa, I, dev, steps, warm):
+    """The two small maps (8x8 in float32, 20x20 in bf16), fused forward and forward + backward,
+    which are bound by launch cost, not by the GPU's arithmetic: an event pair around each step,
+    steps back to back, and 32 steps captured in one HIP graph and replayed (the GPU-side time
+    of a step without the host's launches pacing it)."""
+    res = {}
+    for name, tag in (("psa_fwd_f32_tiny_8x8", "8x8_f32"), ("psa_fwd_bf16_20x20", "20x20")):
+        w = I.WORKLOADS[name]
+        x = I.make_workload_qkv(w).to(dev)
+        shape = (w.B, w.out_channels, w.H, w.W)
+        out, v, dout = (torch.empty(shape, dtype=x.dtype, device=dev) for _ in range(3))
+        dout.copy_(torch.randn(shape, generator=torch.Generator(device=dev).manual_seed(9), device=dev))
+        lse = torch.empty((w.BH, w.N), dtype=torch.float32, device=dev)
+        dqkv = torch.empty_like(x)
+        nb = psa.psa_attention_fwd_workspace_bytes(w.B, w.heads, w.key_dim, w.H, w.W, dtype=x.dtype)
+        ws_f = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev) if nb else None
+        ws_b = torch.empty((max(psa.load_library().psa_attention_bwd_workspace_bytes(w.B, w.heads, w.H, w.W), 4) // 4,),
+                           dtype=torch.float32, device=dev)
+        fwd = lambda _i=0: psa.psa_attention_fwd(x, w.heads, w.key_dim, out=out, v_out=v, lse=lse, workspace=ws_f)
+
+        def fwd_bwd(_i=0):
+            fwd()
+            psa.psa_attention_bwd(x, out, lse, dout, w.heads, w.key_dim, dv=dout, dqkv=dqkv, workspace=ws_b)
+
+        for label, fn, flops in (("fused_fwd", fwd, fwd_flops(w.BH, w.N, w.key_dim)),
+                                 ("fused_fwd_bwd", fwd_bwd, (6.0 + 14.0) * w.BH * w.N ** 2 * w.key_dim)):
+            avg, _, _ = time_events(fn, steps, warm, torch)
+            bb = back_to_back(fn, steps, torch)
+            gr = time_graph([fn] * 32, steps, warm, torch)
+            res[f"{label}_{tag}"] = {
+                "avg_us_event_pair": round(1e3 * avg, 2), "back_to_back_us": round(1e3 * bb, 2),
+                "graph_replay_us": round(1e3 * gr, 2),
+                "TFLOP/s_graph_replay": round(flops / (gr * 1e-3) / 1e12, 3),
+                "note": "launch-bound map; %s flops per step" % ("6*BH*N^2*KD" if label == "fused_fwd" else "(6+14)*BH*N^2*KD")}
+        del x, out, v, dout, lse, dqkv, ws_f, ws_b
+    return res
 
 
 def psa_bwd_component(torch, psa, I, dev, steps, warm):

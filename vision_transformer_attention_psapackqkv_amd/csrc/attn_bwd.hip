@@ -876,15 +876,21 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32(BwdArgs a) {
     vr[d] = ok ? reinterpret_cast<const float*>(a.v)[krow + d] : 0.0f;
     dk[d] = dv[d] = 0.0f;
   }
+  // Thread element i of a [kF32Rows, D] tile: row e / D, column e % D.
+  auto rc = [](int i, int& r, int& d) {
+    const int e = static_cast<int>(threadIdx.x) + i * kF32Threads;
+    r = e / D;
+    d = e % D;
+  };
   for (int q0 = 0; q0 < a.n_q; q0 += kF32Rows) {
     __syncthreads();
-    for (int e = threadIdx.x; e < kF32Rows * D; e += kF32Threads) {
-      const int r = e / D, d = e % D;
-      const bool in = q0 + r < a.n_q;
-      const int64_t i = (static_cast<int64_t>(bh) * a.n_q + q0 + r) * D + d;
-      qs[r][d] = in ? Q[i] : 0.0f;
-      gs[r][d] = in ? G[i] : 0.0f;
-    }
+    auto at = [&](int r, int d) { return (static_cast<int64_t>(bh) * a.n_q + q0 + r) * D + d; };
+    move_batched<kF32Rows * D / kF32Threads>(
+        [&](int i) { int r, d; rc(i, r, d); return q0 + r < a.n_q ? Q[at(r, d)] : 0.0f; },
+        [&](int i, float x) { int r, d; rc(i, r, d); qs[r][d] = x; });
+    move_batched<kF32Rows * D / kF32Threads>(
+        [&](int i) { int r, d; rc(i, r, d); return q0 + r < a.n_q ? G[at(r, d)] : 0.0f; },
+        [&](int i, float x) { int r, d; rc(i, r, d); gs[r][d] = x; });
     if (threadIdx.x < kF32Rows) {
       const int r = threadIdx.x;
       const bool in = q0 + r < a.n_q;
@@ -894,12 +900,8 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32(BwdArgs a) {
     __syncthreads();
     const int cnt = min(kF32Rows, a.n_q - q0);
     for (int r = 0; r < cnt; ++r) {
-      float s = 0.0f, dp = 0.0f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        s = fmaf(qs[r][d], kr[d], s);
-        dp = fmaf(gs[r][d], vr[d], dp);
-      }
+      const float s = dot_f32<D>(qs[r], kr);
+      const float dp = dot_f32<D>(gs[r], vr);
       const float p = expf(s * a.scale - ls[r]);
       const float ds = p * (dp + dls[r]);   // dls holds -Delta
 #pragma unroll
@@ -938,24 +940,25 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dq_f32(BwdArgs a) {
   }
   const float lse = ok ? a.lse[static_cast<int64_t>(bh) * a.n_q + q] : 0.0f;
   const float dl = ok ? a.delta[static_cast<int64_t>(bh) * a.n_q + q] : 0.0f;
+  auto rc = [](int i, int& r, int& d) {
+    const int e = static_cast<int>(threadIdx.x) + i * kF32Threads;
+    r = e / D;
+    d = e % D;
+  };
   for (int m0 = 0; m0 < a.n_k; m0 += kF32Rows) {
     __syncthreads();
-    for (int e = threadIdx.x; e < kF32Rows * D; e += kF32Threads) {
-      const int r = e / D, d = e % D;
-      const bool in = m0 + r < a.n_k;
-      const int64_t i = (static_cast<int64_t>(bh) * a.n_k + m0 + r) * D + d;
-      ks[r][d] = in ? K[i] : 0.0f;
-      vs[r][d] = in ? V[i] : 0.0f;
-    }
+    auto at = [&](int r, int d) { return (static_cast<int64_t>(bh) * a.n_k + m0 + r) * D + d; };
+    move_batched<kF32Rows * D / kF32Threads>(
+        [&](int i) { int r, d; rc(i, r, d); return m0 + r < a.n_k ? K[at(r, d)] : 0.0f; },
+        [&](int i, float x) { int r, d; rc(i, r, d); ks[r][d] = x; });
+    move_batched<kF32Rows * D / kF32Threads>(
+        [&](int i) { int r, d; rc(i, r, d); return m0 + r < a.n_k ? V[at(r, d)] : 0.0f; },
+        [&](int i, float x) { int r, d; rc(i, r, d); vs[r][d] = x; });
     __syncthreads();
     const int cnt = min(kF32Rows, a.n_k - m0);
     for (int r = 0; r < cnt; ++r) {
-      float s = 0.0f, dp = 0.0f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        s = fmaf(qr[d], ks[r][d], s);
-        dp = fmaf(gr[d], vs[r][d], dp);
-      }
+      const float s = dot_f32<D>(qr, ks[r]);
+      const float dp = dot_f32<D>(gr, vs[r]);
       const float ds = expf(s * a.scale - lse) * (dp + dl);   // dl = -Delta
 #pragma unroll
       for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, ks[r][d], dq[d]);

@@ -847,10 +847,12 @@ struct FwdArgsF32 {
 };
 
 constexpr int kF32Threads = 128;
-constexpr int kF32Keys = 32;
+constexpr int kF32Keys = 32;   // keys per LDS tile
+constexpr int kF32Sub = 8;     // keys per softmax group
 
 // One thread per query row, keys staged through LDS in tiles of 32, float32
-// throughout with expf. The fused (NCHW) variant computes the softmax once and
+// throughout with expf; the online softmax moves its maximum once per group of
+// 8 keys (whose scores are computed side by side), not once per key. The fused (NCHW) variant computes the softmax once and
 // multiplies P by both V halves, [V_lo | V_hi] (value width 2*KD), as the bf16
 // kernel does, up to key_dim 64; at key_dim 128 (a 256-wide accumulator per
 // thread would not fit the registers) workgroups take one V half each and the
@@ -904,29 +906,45 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
       vs[r][d] = m0 + r < a.n_k ? a.v[vi(m0 + r, d)] : 0.0f;
     }
     __syncthreads();
+    // The tile's keys in groups of kF32Sub: the group's scores are independent
+    // dot products (computed side by side), then one rescale of O and the row
+    // sum by the group's new maximum, then P times the group's V rows.
     const int cnt = min(kF32Keys, a.n_k - m0);
-    for (int r = 0; r < cnt; ++r) {
-      float s = 0.0f;
+    for (int r0 = 0; r0 < cnt; r0 += kF32Sub) {
+      float sc[kF32Sub];
+      float mt = m;
 #pragma unroll
-      for (int d = 0; d < KD; ++d) s = fmaf(q[d], ks[r][d], s);
-      s *= a.scale;
-      const float m_new = fmaxf(m, s);
-      const float alpha = expf(m - m_new);
-      const float p = expf(s - m_new);
-      l = l * alpha + p;
+      for (int u = 0; u < kF32Sub; ++u) {
+        float s = 0.0f;
 #pragma unroll
-      for (int d = 0; d < VW; ++d) o[d] = fmaf(p, vs[r][d], o[d] * alpha);
-      m = m_new;
+        for (int d = 0; d < KD; ++d) s = fmaf(q[d], ks[r0 + u][d], s);
+        sc[u] = r0 + u < cnt ? s * a.scale : -INFINITY;   // keys past n_k: P = 0
+        mt = fmaxf(mt, sc[u]);
+      }
+      const float alpha = expf(m - mt);   // 0 on the first group (m = -inf)
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < VW; ++d) o[d] *= alpha;
+#pragma unroll
+      for (int u = 0; u < kF32Sub; ++u) {
+        const float p = expf(sc[u] - mt);
+        l += p;
+#pragma unroll
+        for (int d = 0; d < VW; ++d) o[d] = fmaf(p, vs[r0 + u][d], o[d]);
+      }
+      m = mt;
     }
   }
   if (!ok) return;
   const float inv = 1.0f / l;
+  auto oi = [&](int d) -> int64_t {
+    return kNCHW ? (static_cast<int64_t>(bh) * 2 * KD + j * KD + d) * N + row
+                 : (static_cast<int64_t>(bh) * a.n_q + row) * KD + d;
+  };
 #pragma unroll
   for (int d = 0; d < VW; ++d) {
-    const int64_t oi = kNCHW ? (static_cast<int64_t>(bh) * 2 * KD + j * KD + d) * N + row
-                             : (static_cast<int64_t>(bh) * a.n_q + row) * KD + d;
-    a.o[oi] = o[d] * inv;
-    if (kNCHW && a.vres != nullptr) a.vres[oi] = a.v[vi(row, d)];
+    a.o[oi(d)] = o[d] * inv;
+    if (kNCHW && a.vres != nullptr) a.vres[oi(d)] = a.v[vi(row, d)];
   }
   if (a.lse != nullptr && j == 0) a.lse[static_cast<int64_t>(bh) * a.n_q + row] = m + logf(l);
 }

@@ -583,6 +583,14 @@ struct PsaBwdF32Args {
 constexpr int kF32Threads = 128;   // one row per thread
 constexpr int kF32Rows = 32;       // rows per LDS tile
 
+// Thread element i of a [kF32Rows][cols] LDS tile filled from channel rows:
+// pixels (tile rows) fastest, as they are contiguous in NCHW.
+__device__ __forceinline__ void f32_rc(int i, int& r, int& d) {
+  const int e = static_cast<int>(threadIdx.x) + i * kF32Threads;
+  r = e % kF32Rows;
+  d = e / kF32Rows;
+}
+
 // -Delta_j = -sum over half j's channels of dO * O, one thread per pixel.
 __global__ __launch_bounds__(256) void psa_bwd_delta_f32(PsaBwdF32Args a) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -591,6 +599,7 @@ __global__ __launch_bounds__(256) void psa_bwd_delta_f32(PsaBwdF32Args a) {
   const int n = static_cast<int>(i - static_cast<int64_t>(bh) * a.N);
   const int64_t base = (static_cast<int64_t>(bh) * 2 * a.KD + a.j * a.KD) * a.N + n;
   float s = 0.0f;
+#pragma unroll 8
   for (int c = 0; c < a.KD; ++c) s = fmaf(a.dout[base + static_cast<int64_t>(c) * a.N], a.o[base + static_cast<int64_t>(c) * a.N], s);
   a.delta[i] = -s;
 }
@@ -618,12 +627,12 @@ __global__ __launch_bounds__(kF32Threads) void psa_bwd_dkdv_f32(PsaBwdF32Args a)
   }
   for (int q0 = 0; q0 < N; q0 += kF32Rows) {
     __syncthreads();
-    for (int e = threadIdx.x; e < kF32Rows * KD; e += kF32Threads) {
-      const int r = e % kF32Rows, d = e / kF32Rows;
-      const bool in = q0 + r < N;
-      qs[r][d] = in ? Q[static_cast<int64_t>(d) * N + q0 + r] : 0.0f;
-      gs[r][d] = in ? G[static_cast<int64_t>(d) * N + q0 + r] : 0.0f;
-    }
+    move_batched<kF32Rows * KD / kF32Threads>(
+        [&](int i) { int r, d; f32_rc(i, r, d); return q0 + r < N ? Q[static_cast<int64_t>(d) * N + q0 + r] : 0.0f; },
+        [&](int i, float x) { int r, d; f32_rc(i, r, d); qs[r][d] = x; });
+    move_batched<kF32Rows * KD / kF32Threads>(
+        [&](int i) { int r, d; f32_rc(i, r, d); return q0 + r < N ? G[static_cast<int64_t>(d) * N + q0 + r] : 0.0f; },
+        [&](int i, float x) { int r, d; f32_rc(i, r, d); gs[r][d] = x; });
     if (threadIdx.x < kF32Rows) {
       const int r = threadIdx.x;
       const bool in = q0 + r < N;
@@ -633,12 +642,8 @@ __global__ __launch_bounds__(kF32Threads) void psa_bwd_dkdv_f32(PsaBwdF32Args a)
     __syncthreads();
     const int cnt = min(kF32Rows, N - q0);
     for (int r = 0; r < cnt; ++r) {
-      float sc = 0.0f, dp = 0.0f;
-#pragma unroll
-      for (int d = 0; d < KD; ++d) {
-        sc = fmaf(qs[r][d], kr[d], sc);
-        dp = fmaf(gs[r][d], vr[d], dp);
-      }
+      const float sc = dot_f32<KD>(qs[r], kr);
+      const float dp = dot_f32<KD>(gs[r], vr);
       const float p = expf(sc * a.scale - ls[r]);
       const float ds = p * (dp + dls[r]);   // dls holds -Delta_j
 #pragma unroll
@@ -651,11 +656,21 @@ __global__ __launch_bounds__(kF32Threads) void psa_bwd_dkdv_f32(PsaBwdF32Args a)
   if (!ok) return;
   float* out = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N;
   const float* res = a.dvres ? a.dvres + (static_cast<int64_t>(bh) * 2 + a.j) * KD * N : nullptr;
+  float* pk = out + static_cast<int64_t>(KD) * N + m;             // dK channel rows
+  float* pv = out + static_cast<int64_t>(2 + a.j) * KD * N + m;   // dV_j channel rows
+  if (a.j == 0) {
 #pragma unroll
-  for (int d = 0; d < KD; ++d) {
-    float* pk = out + static_cast<int64_t>(KD + d) * N + m;
-    *pk = a.j == 0 ? dk[d] * a.scale : *pk + dk[d] * a.scale;
-    out[static_cast<int64_t>((2 + a.j) * KD + d) * N + m] = res ? dv[d] + res[static_cast<int64_t>(d) * N + m] : dv[d];
+    for (int d = 0; d < KD; ++d) pk[static_cast<int64_t>(d) * N] = dk[d] * a.scale;
+  } else {
+    move_batched<KD>([&](int d) { return pk[static_cast<int64_t>(d) * N]; },
+                     [&](int d, float x) { pk[static_cast<int64_t>(d) * N] = x + dk[d] * a.scale; });
+  }
+  if (res) {
+    move_batched<KD>([&](int d) { return res[static_cast<int64_t>(d) * N + m]; },
+                     [&](int d, float x) { pv[static_cast<int64_t>(d) * N] = dv[d] + x; });
+  } else {
+#pragma unroll
+    for (int d = 0; d < KD; ++d) pv[static_cast<int64_t>(d) * N] = dv[d];
   }
 }
 
@@ -683,32 +698,34 @@ __global__ __launch_bounds__(kF32Threads) void psa_bwd_dq_f32(PsaBwdF32Args a) {
   const float dl = a.delta[static_cast<int64_t>(bh) * N + nc];   // -Delta_j
   for (int m0 = 0; m0 < N; m0 += kF32Rows) {
     __syncthreads();
-    for (int e = threadIdx.x; e < kF32Rows * KD; e += kF32Threads) {
-      const int r = e % kF32Rows, d = e / kF32Rows;
-      const bool in = m0 + r < N;
-      ks[r][d] = in ? Q[static_cast<int64_t>(KD + d) * N + m0 + r] : 0.0f;
-      vs[r][d] = in ? Q[static_cast<int64_t>((2 + a.j) * KD + d) * N + m0 + r] : 0.0f;
-    }
+    move_batched<kF32Rows * KD / kF32Threads>(
+        [&](int i) { int r, d; f32_rc(i, r, d); return m0 + r < N ? Q[static_cast<int64_t>(KD + d) * N + m0 + r] : 0.0f; },
+        [&](int i, float x) { int r, d; f32_rc(i, r, d); ks[r][d] = x; });
+    move_batched<kF32Rows * KD / kF32Threads>(
+        [&](int i) {
+          int r, d;
+          f32_rc(i, r, d);
+          return m0 + r < N ? Q[static_cast<int64_t>((2 + a.j) * KD + d) * N + m0 + r] : 0.0f;
+        },
+        [&](int i, float x) { int r, d; f32_rc(i, r, d); vs[r][d] = x; });
     __syncthreads();
     const int cnt = min(kF32Rows, N - m0);
     for (int r = 0; r < cnt; ++r) {
-      float sc = 0.0f, dp = 0.0f;
-#pragma unroll
-      for (int d = 0; d < KD; ++d) {
-        sc = fmaf(qr[d], ks[r][d], sc);
-        dp = fmaf(gr[d], vs[r][d], dp);
-      }
+      const float sc = dot_f32<KD>(qr, ks[r]);
+      const float dp = dot_f32<KD>(gr, vs[r]);
       const float ds = expf(sc * a.scale - lse) * (dp + dl);
 #pragma unroll
       for (int d = 0; d < KD; ++d) dq[d] = fmaf(ds, ks[r][d], dq[d]);
     }
   }
   if (!ok) return;
-  float* out = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N;
+  float* p = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N + n;   // dQ channel rows
+  if (a.j == 0) {
 #pragma unroll
-  for (int d = 0; d < KD; ++d) {
-    float* p = out + static_cast<int64_t>(d) * N + n;
-    *p = a.j == 0 ? dq[d] * a.scale : *p + dq[d] * a.scale;
+    for (int d = 0; d < KD; ++d) p[static_cast<int64_t>(d) * N] = dq[d] * a.scale;
+  } else {
+    move_batched<KD>([&](int d) { return p[static_cast<int64_t>(d) * N]; },
+                     [&](int d, float x) { p[static_cast<int64_t>(d) * N] = x + dq[d] * a.scale; });
   }
 }
 

@@ -133,4 +133,35 @@ __device__ __forceinline__ T ldg_nt(const T* p) { return __builtin_nontemporal_l
 template <typename T>
 __device__ __forceinline__ void stg_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
 
+// Moves E float32 values per thread between global memory and LDS (or from
+// one global buffer to another) for the one-thread-per-row float32 kernels:
+// the loads of each batch of up to 8 are issued before the batch's stores, so
+// a thread waits for memory once per batch rather than once per value (a load
+// followed by a store that may alias the next load would otherwise be waited
+// for one at a time). load(i) returns the thread's i-th value, store(i, x)
+// writes it.
+template <int E, typename Load, typename Store>
+__device__ __forceinline__ void move_batched(Load&& load, Store&& store) {
+  constexpr int kB = E < 8 ? E : 8;
+  static_assert(E % kB == 0, "whole batches");
+#pragma unroll
+  for (int i0 = 0; i0 < E; i0 += kB) {
+    float t[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) t[i] = load(i0 + i);
+#pragma unroll
+    for (int i = 0; i < kB; ++i) store(i0 + i, t[i]);
+  }
+}
+
+// Dot product of two float32 rows of D values as four partial sums (by d mod
+// 4): four independent chains of multiply-adds instead of one.
+template <int D>
+__device__ __forceinline__ float dot_f32(const float* x, const float* y) {
+  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int d = 0; d < D; ++d) s[d & 3] = fmaf(x[d], y[d], s[d & 3]);
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
 }  // namespace psa
