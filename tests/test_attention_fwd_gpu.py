@@ -24,6 +24,14 @@ FA2_SHAPES = [
     (3, 100, 77, 32, "f32"),
     (2, 33, 130, 64, "f32"),
     (1, 20, 45, 128, "f32"),
+    # float32 with fewer keys than a row's four lanes (lanes that never see a key), and
+    # key counts that end a 32-key tile after 1..3 of a lane's keys
+    (2, 37, 1, 16, "f32"),
+    (1, 5, 2, 32, "f32"),
+    (2, 70, 3, 64, "f32"),
+    (1, 33, 5, 128, "f32"),
+    (3, 45, 34, 16, "f32"),
+    (2, 31, 67, 64, "f32"),
 ]
 
 
@@ -56,6 +64,9 @@ PSA_SHAPES = [
     (1, 2, 32, 3, 3, "f32"),
     (1, 1, 64, 10, 13, "f32"),
     (1, 1, 128, 4, 6, "f32"),
+    (1, 2, 16, 1, 1, "f32"),            # one pixel in float32: O = V
+    (2, 1, 32, 1, 3, "f32"),            # N = 3: a row's fourth lane sees no key
+    (1, 1, 64, 5, 7, "f32"),            # N = 35: a second tile of 3 keys
 ]
 
 

@@ -45,6 +45,7 @@
 // product and the row sum adds the same rounded values.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -844,20 +845,26 @@ struct FwdArgsF32 {
   float* lse;
   int BH, n_q, n_k;
   float scale;
+  int bh0;   // first batch-head of this launch
 };
 
 constexpr int kF32Threads = 128;
-constexpr int kF32Keys = 32;   // keys per LDS tile
-constexpr int kF32Sub = 8;     // keys per softmax group
+constexpr int kF32Keys = 32;                          // keys per LDS tile
+constexpr int kF32Lanes = 4;                          // lanes per query row
+constexpr int kF32Rows = kF32Threads / kF32Lanes;     // query rows per workgroup
+constexpr int kF32Sub = kF32Keys / kF32Lanes;         // keys per lane and tile
 
-// One thread per query row, keys staged through LDS in tiles of 32, float32
-// throughout with expf; the online softmax moves its maximum once per group of
-// 8 keys (whose scores are computed side by side), not once per key. The fused (NCHW) variant computes the softmax once and
-// multiplies P by both V halves, [V_lo | V_hi] (value width 2*KD), as the bf16
-// kernel does, up to key_dim 64; at key_dim 128 (a 256-wide accumulator per
-// thread would not fit the registers) workgroups take one V half each and the
-// softmax is computed once per half. Workgroups enumerate (bh, V part, query
-// block).
+// Four lanes per query row, keys staged through LDS in tiles of 32, float32
+// throughout with expf. Lane l of a row takes keys l, l+4, ... of every tile
+// and keeps its own online softmax (maximum, row sum, accumulator); its 8 keys
+// of a tile are scored side by side and the maximum moves once per tile. The
+// four partial softmaxes of a row are combined at the end (lane exchanges
+// within the group of four), and each lane stores a quarter of the columns.
+// The fused (NCHW) variant computes the softmax once and multiplies P by both
+// V halves, [V_lo | V_hi] (value width 2*KD), as the bf16 kernel does, up to
+// key_dim 64; at key_dim 128 (a 256-wide accumulator per lane would not fit
+// the registers) workgroups take one V half each and the softmax is computed
+// once per half. Workgroups enumerate (bh, V part, query block).
 template <int KD, bool kNCHW>
 constexpr int f32_parts() { return kNCHW && KD > 64 ? 2 : 1; }   // workgroups per (bh, query block)
 
@@ -867,11 +874,12 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
   constexpr int VW = kNCHW && kParts == 1 ? 2 * KD : KD;   // value columns per workgroup
   __shared__ float ks[kF32Keys][KD];
   __shared__ float vs[kF32Keys][VW];
-  const int q_blocks = (a.n_q + kF32Threads - 1) / kF32Threads;
+  const int q_blocks = (a.n_q + kF32Rows - 1) / kF32Rows;
   const int qb = blockIdx.x % q_blocks;
-  const int bh = (blockIdx.x / q_blocks) / kParts;
+  const int bh = a.bh0 + static_cast<int>((blockIdx.x / q_blocks) / kParts);
   const int j = (blockIdx.x / q_blocks) % kParts;
-  const int row = qb * kF32Threads + threadIdx.x;
+  const int lane = threadIdx.x % kF32Lanes;
+  const int row = qb * kF32Rows + threadIdx.x / kF32Lanes;
   const bool ok = row < a.n_q;
   const int N = a.n_k;
   // Element (row n, column d) of Q, K and this workgroup's V columns, in either layout.
@@ -906,34 +914,46 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
       vs[r][d] = m0 + r < a.n_k ? a.v[vi(m0 + r, d)] : 0.0f;
     }
     __syncthreads();
-    // The tile's keys in groups of kF32Sub: the group's scores are independent
-    // dot products (computed side by side), then one rescale of O and the row
-    // sum by the group's new maximum, then P times the group's V rows.
+    // This lane's keys of the tile, lane + 4u: independent dot products, then
+    // one rescale of O and the row sum by the new maximum, then P times V.
     const int cnt = min(kF32Keys, a.n_k - m0);
-    for (int r0 = 0; r0 < cnt; r0 += kF32Sub) {
-      float sc[kF32Sub];
-      float mt = m;
+    float sc[kF32Sub];
+    float mt = m;
 #pragma unroll
-      for (int u = 0; u < kF32Sub; ++u) {
-        float s = 0.0f;
+    for (int u = 0; u < kF32Sub; ++u) {
+      const int r = lane + kF32Lanes * u;
+      float s = 0.0f;
 #pragma unroll
-        for (int d = 0; d < KD; ++d) s = fmaf(q[d], ks[r0 + u][d], s);
-        sc[u] = r0 + u < cnt ? s * a.scale : -INFINITY;   // keys past n_k: P = 0
-        mt = fmaxf(mt, sc[u]);
-      }
-      const float alpha = expf(m - mt);   // 0 on the first group (m = -inf)
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < VW; ++d) o[d] *= alpha;
-#pragma unroll
-      for (int u = 0; u < kF32Sub; ++u) {
-        const float p = expf(sc[u] - mt);
-        l += p;
-#pragma unroll
-        for (int d = 0; d < VW; ++d) o[d] = fmaf(p, vs[r0 + u][d], o[d]);
-      }
-      m = mt;
+      for (int d = 0; d < KD; ++d) s = fmaf(q[d], ks[r][d], s);
+      sc[u] = r < cnt ? s * a.scale : -INFINITY;   // keys past n_k: P = 0
+      mt = fmaxf(mt, sc[u]);
     }
+    if (mt == -INFINITY) continue;       // no key of this lane yet
+    const float alpha = expf(m - mt);    // 0 while m = -inf
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < VW; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kF32Sub; ++u) {
+      const float p = expf(sc[u] - mt);
+      l += p;
+#pragma unroll
+      for (int d = 0; d < VW; ++d) o[d] = fmaf(p, vs[lane + kF32Lanes * u][d], o[d]);
+    }
+    m = mt;
+  }
+  // Combine the row's four partial softmaxes (a lane with no key has m = -inf, l = 0, O = 0).
+#pragma unroll
+  for (int x = 1; x < kF32Lanes; x <<= 1) {
+    const float mo = __shfl_xor(m, x);
+    const float lo = __shfl_xor(l, x);
+    const float mn = fmaxf(m, mo);
+    const float a0 = m == -INFINITY ? 0.0f : expf(m - mn);
+    const float a1 = mo == -INFINITY ? 0.0f : expf(mo - mn);
+    l = l * a0 + lo * a1;
+#pragma unroll
+    for (int d = 0; d < VW; ++d) o[d] = o[d] * a0 + __shfl_xor(o[d], x) * a1;
+    m = mn;
   }
   if (!ok) return;
   const float inv = 1.0f / l;
@@ -941,12 +961,15 @@ __global__ __launch_bounds__(kF32Threads) void attn_fwd_f32(FwdArgsF32 a) {
     return kNCHW ? (static_cast<int64_t>(bh) * 2 * KD + j * KD + d) * N + row
                  : (static_cast<int64_t>(bh) * a.n_q + row) * KD + d;
   };
+  // Each lane stores the columns d = lane (mod 4).
 #pragma unroll
   for (int d = 0; d < VW; ++d) {
+    if (d % kF32Lanes != lane) continue;
     a.o[oi(d)] = o[d] * inv;
     if (kNCHW && a.vres != nullptr) a.vres[oi(d)] = a.v[vi(row, d)];
   }
-  if (a.lse != nullptr && j == 0) a.lse[static_cast<int64_t>(bh) * a.n_q + row] = m + logf(l);
+  if (a.lse != nullptr && j == 0 && lane == 0)
+    a.lse[static_cast<int64_t>(bh) * a.n_q + row] = m + logf(l);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -1111,10 +1134,18 @@ size_t split_bytes(int BH, int n_q, int n_k, bool vec_n) {
 
 template <int KD, bool kNCHW>
 hipError_t run_f32(FwdArgsF32 a, hipStream_t stream) {
-  const unsigned q_blocks = (a.n_q + kF32Threads - 1) / kF32Threads;
-  const dim3 grid(q_blocks * a.BH * f32_parts<KD, kNCHW>());
-  attn_fwd_f32<KD, kNCHW><<<grid, kF32Threads, 0, stream>>>(a);
-  return hipGetLastError();
+  const int64_t per_bh = static_cast<int64_t>((a.n_q + kF32Rows - 1) / kF32Rows) * f32_parts<KD, kNCHW>();
+  // A launch holds at most 2^31 work-items: batch-heads in as many launches as that takes.
+  const int64_t max_bh = std::max<int64_t>(1, (int64_t(1) << 31) / (per_bh * kF32Threads));
+  for (int64_t b0 = 0; b0 < a.BH; b0 += max_bh) {
+    FwdArgsF32 c = a;
+    c.bh0 = static_cast<int>(b0);
+    const int64_t nb = std::min<int64_t>(max_bh, a.BH - b0);
+    attn_fwd_f32<KD, kNCHW><<<dim3(static_cast<unsigned>(per_bh * nb)), kF32Threads, 0, stream>>>(c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
