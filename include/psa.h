@@ -163,7 +163,9 @@ size_t fa2_bwd_workspace_bytes(int BH, int n_q);
  * argument. The -Delta and LSE * log2(e) rows live instead in a scratch array of
  * PSA_NOALLOC_SCRATCH_BYTES that the library's code object holds in device
  * memory; each GPU it runs on has its own copy, held until the process ends.
- * The entry point calls no allocating routine. Limit: BH * n_q <=
+ * Its device address is looked up once per GPU, by the first call of any
+ * entry point on that GPU, before that call launches anything. The entry
+ * point calls no allocating routine. Limit: BH * n_q <=
  * PSA_NOALLOC_SCRATCH_BYTES / 8 (2,097,152 rows); larger calls return
  * PSA_ERR_SHAPE before anything is launched (use fa2_bwd with a workspace).
  * Every call on one GPU shares that scratch: calls whose executions overlap

@@ -22,6 +22,12 @@ SHAPES = [
     (3, 100, 77, 32, "f32"),
     (2, 33, 130, 64, "f32"),
     (1, 20, 45, 128, "f32"),
+    # float32 with fewer keys or queries than a row's four lanes, and tiles that end after
+    # 1..3 of a lane's rows
+    (2, 37, 1, 16, "f32"),
+    (1, 2, 70, 32, "f32"),
+    (2, 3, 5, 64, "f32"),
+    (1, 35, 33, 128, "f32"),
 ]
 
 

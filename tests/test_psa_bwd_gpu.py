@@ -171,7 +171,9 @@ def test_psa_attention_bwd_zero_queries(kd):
 
 # float32 (PSA_F32): the VALU path, one V half after the other. Every key_dim, N a multiple of
 # 8 or not, with and without the V-residual gradient; float32 tolerance against the oracle.
-F32_SHAPES = [(1, 2, 16, 8, 8), (2, 1, 32, 7, 9), (1, 2, 64, 10, 13), (1, 1, 128, 9, 12), (1, 1, 16, 1, 1)]
+# ... and N = 3 (a pixel's fourth lane sees no query or key) and N = 35 (a second tile of 3)
+F32_SHAPES = [(1, 2, 16, 8, 8), (2, 1, 32, 7, 9), (1, 2, 64, 10, 13), (1, 1, 128, 9, 12), (1, 1, 16, 1, 1),
+              (2, 1, 32, 1, 3), (1, 2, 64, 5, 7)]
 
 
 @pytest.mark.parametrize("with_dv", [False, True], ids=["no_dv", "dv"])

@@ -21,9 +21,11 @@
 // rows, are read from the same row tiles with transposed LDS reads
 // (ds_read_b64_tr_b16). Head dims 32..128 stage their tiles straight from
 // global memory into swizzled unpadded rows; head dim 16 through registers
-// into padded rows. The float32 path is one thread per row on the VALU.
+// into padded rows. The float32 path runs on the VALU, four lanes per row.
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -51,6 +53,7 @@ struct BwdArgs {
   int tiles;            // workgroups per batch-head
   float scale;
   float c;              // scale * log2(e)
+  int bh0;              // float32 kernels: first batch-head of this launch
 };
 
 
@@ -854,9 +857,23 @@ __global__ __launch_bounds__(kWaves * 64, D <= 32 ? 4 : D == 64 ? 2 : 1) void bw
 // ---------------------------------------------------------------- float32
 
 constexpr int kF32Threads = 128;
-constexpr int kF32Rows = 32;
+constexpr int kF32Rows = 32;                        // rows per LDS tile
+constexpr int kF32Lanes = 4;                        // lanes per output row
+constexpr int kF32Out = kF32Threads / kF32Lanes;    // output rows per workgroup
 
-// dK/dV: one thread per key, queries staged through LDS.
+// Adds the partial sums x[0..D) of the four lanes of an output row (lanes
+// 4i..4i+3); every lane ends with the total.
+template <int D>
+__device__ __forceinline__ void sum_lanes(float (&x)[D]) {
+#pragma unroll
+  for (int m = 1; m < kF32Lanes; m <<= 1)
+#pragma unroll
+    for (int d = 0; d < D; ++d) x[d] += __shfl_xor(x[d], m);
+}
+
+// dK/dV: four lanes per key, lane l taking queries l, l+4, ... of each tile
+// (staged through LDS); the lanes' partial dK and dV are added at the end and
+// each lane stores the columns d = l (mod 4).
 template <int D>
 __global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32(BwdArgs a) {
   __shared__ float qs[kF32Rows][D];
@@ -864,9 +881,10 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32(BwdArgs a) {
   __shared__ float ls[kF32Rows], dls[kF32Rows];
   const float* Q = reinterpret_cast<const float*>(a.q);
   const float* G = reinterpret_cast<const float*>(a.dout);
-  const int blocks = (a.n_k + kF32Threads - 1) / kF32Threads;
-  const int bh = blockIdx.x / blocks;
-  const int key = (blockIdx.x % blocks) * kF32Threads + threadIdx.x;
+  const int blocks = (a.n_k + kF32Out - 1) / kF32Out;
+  const int bh = a.bh0 + static_cast<int>(blockIdx.x / blocks);
+  const int lane = threadIdx.x % kF32Lanes;
+  const int key = (blockIdx.x % blocks) * kF32Out + threadIdx.x / kF32Lanes;
   const bool ok = key < a.n_k;
   float kr[D], vr[D], dk[D], dv[D];
   const int64_t krow = (static_cast<int64_t>(bh) * a.n_k + (ok ? key : 0)) * D;
@@ -899,7 +917,7 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32(BwdArgs a) {
     }
     __syncthreads();
     const int cnt = min(kF32Rows, a.n_q - q0);
-    for (int r = 0; r < cnt; ++r) {
+    for (int r = lane; r < cnt; r += kF32Lanes) {
       const float s = dot_f32<D>(qs[r], kr);
       const float dp = dot_f32<D>(gs[r], vr);
       const float p = expf(s * a.scale - ls[r]);
@@ -911,24 +929,29 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dkdv_f32(BwdArgs a) {
       }
     }
   }
+  sum_lanes<D>(dk);
+  sum_lanes<D>(dv);
   if (!ok) return;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
+    if (d % kF32Lanes != lane) continue;
     reinterpret_cast<float*>(a.dk)[krow + d] = dk[d] * a.scale;
     reinterpret_cast<float*>(a.dv)[krow + d] = dv[d];
   }
 }
 
-// dQ: one thread per query, keys staged through LDS.
+// dQ: four lanes per query, lane l taking keys l, l+4, ... of each tile; the
+// lanes' partial dQ are added at the end.
 template <int D>
 __global__ __launch_bounds__(kF32Threads) void bwd_dq_f32(BwdArgs a) {
   __shared__ float ks[kF32Rows][D];
   __shared__ float vs[kF32Rows][D];
   const float* K = reinterpret_cast<const float*>(a.k);
   const float* V = reinterpret_cast<const float*>(a.v);
-  const int blocks = (a.n_q + kF32Threads - 1) / kF32Threads;
-  const int bh = blockIdx.x / blocks;
-  const int q = (blockIdx.x % blocks) * kF32Threads + threadIdx.x;
+  const int blocks = (a.n_q + kF32Out - 1) / kF32Out;
+  const int bh = a.bh0 + static_cast<int>(blockIdx.x / blocks);
+  const int lane = threadIdx.x % kF32Lanes;
+  const int q = (blockIdx.x % blocks) * kF32Out + threadIdx.x / kF32Lanes;
   const bool ok = q < a.n_q;
   const int64_t qrow = (static_cast<int64_t>(bh) * a.n_q + (ok ? q : 0)) * D;
   float qr[D], gr[D], dq[D];
@@ -956,7 +979,7 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dq_f32(BwdArgs a) {
         [&](int i, float x) { int r, d; rc(i, r, d); vs[r][d] = x; });
     __syncthreads();
     const int cnt = min(kF32Rows, a.n_k - m0);
-    for (int r = 0; r < cnt; ++r) {
+    for (int r = lane; r < cnt; r += kF32Lanes) {
       const float s = dot_f32<D>(qr, ks[r]);
       const float dp = dot_f32<D>(gr, vs[r]);
       const float ds = expf(s * a.scale - lse) * (dp + dl);   // dl = -Delta
@@ -964,9 +987,28 @@ __global__ __launch_bounds__(kF32Threads) void bwd_dq_f32(BwdArgs a) {
       for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, ks[r][d], dq[d]);
     }
   }
+  sum_lanes<D>(dq);
   if (!ok) return;
 #pragma unroll
-  for (int d = 0; d < D; ++d) reinterpret_cast<float*>(a.dq)[qrow + d] = dq[d] * a.scale;
+  for (int d = 0; d < D; ++d)
+    if (d % kF32Lanes == lane) reinterpret_cast<float*>(a.dq)[qrow + d] = dq[d] * a.scale;
+}
+
+// Launches a float32 kernel of kF32Out output rows per workgroup over `rows`
+// rows per batch-head, in as many launches as keep each at most 2^31 work-items.
+template <typename K>
+hipError_t launch_f32_rows(K kernel, BwdArgs a, int rows, hipStream_t stream) {
+  const int64_t per_bh = (rows + kF32Out - 1) / kF32Out;
+  const int64_t max_bh = std::max<int64_t>(1, (int64_t(1) << 31) / (per_bh * kF32Threads));
+  for (int64_t b0 = 0; b0 < a.BH; b0 += max_bh) {
+    BwdArgs c = a;
+    c.bh0 = static_cast<int>(b0);
+    const int64_t nb = std::min<int64_t>(max_bh, a.BH - b0);
+    kernel<<<dim3(static_cast<unsigned>(per_bh * nb)), kF32Threads, 0, stream>>>(c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -1014,10 +1056,10 @@ hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
     bwd_dq_bf16<D, kWavesBwd><<<grid_q, kWavesBwd * 64, 0, stream>>>(qa);
   } else {
     bwd_delta<D, false><<<grid_delta, 256, 0, stream>>>(a);
-    const unsigned kb = (a.n_k + kF32Threads - 1) / kF32Threads;
-    bwd_dkdv_f32<D><<<dim3(kb * a.BH), kF32Threads, 0, stream>>>(a);
-    const unsigned qb = (a.n_q + kF32Threads - 1) / kF32Threads;
-    bwd_dq_f32<D><<<dim3(qb * a.BH), kF32Threads, 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = launch_f32_rows(bwd_dkdv_f32<D>, a, a.n_k, stream);
+    if (e == hipSuccess) e = launch_f32_rows(bwd_dq_f32<D>, a, a.n_q, stream);
+    return e;
   }
   return hipGetLastError();
 }
@@ -1030,6 +1072,42 @@ hipError_t run(BwdArgs a, bool bf16, hipStream_t stream) {
 // until the process ends; every call on one GPU shares it.
 static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
 
+namespace {
+
+// Device address of `scratch` per device, looked up once with that device
+// current. In host code `scratch` names a host-side stand-in, not the device
+// array: only the looked-up address is passed to kernels.
+std::mutex g_scratch_mu;
+std::atomic<float*> g_scratch_addr[64];
+
+hipError_t scratch_address(float** out) {
+  int dev = 0;
+  const hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  float* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* a = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      p = static_cast<float*>(a);
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t init_device() {
+  float* p = nullptr;
+  return scratch_address(&p);
+}
+
 hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
                                   int BH, int n_q, int n_k, int D, float scale, bool bf16,
@@ -1037,26 +1115,9 @@ hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, c
   if (static_cast<int64_t>(BH) * n_q * static_cast<int64_t>(2 * sizeof(float)) >
       static_cast<int64_t>(kNoAllocScratchBytes))
     return hipErrorInvalidValue;
-  // In host code `scratch` names a host-side stand-in, not the device array:
-  // its device address is looked up once per device, with that device
-  // current, and only that address is passed to the kernels.
-  static std::mutex mu;
-  static float* addr[64] = {};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   float* ws = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    if (addr[dev] == nullptr) {
-      void* p = nullptr;
-      err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-      if (err != hipSuccess) return err;
-      addr[dev] = static_cast<float*>(p);
-    }
-    ws = addr[dev];
-  }
+  const hipError_t err = scratch_address(&ws);
+  if (err != hipSuccess) return err;
   return launch_fa2_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, BH, n_q, n_k, D, scale, bf16,
                         stream);
 }

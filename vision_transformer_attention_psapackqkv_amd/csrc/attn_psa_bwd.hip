@@ -35,13 +35,14 @@
 // (buffer loads with an LDS destination) when N is a multiple of 8, through registers
 // otherwise. Scores use base 2: P = 2^(S * s*log2(e) - LSE*log2(e)).
 //
-// float32 (PSA_F32): one thread per row on the VALU, in float32 with expf, one
+// float32 (PSA_F32): four lanes per row on the VALU, in float32 with expf, one
 // V half at a time. Delta, dS, dQ and dK are linear over the halves (Delta =
 // Delta_lo + Delta_hi, dS = dS_lo + dS_hi with dS_j = P * (dO_j V_j^T -
 // Delta_j)), so each half runs a Delta pass, a dK/dV pass and a dQ pass, and
 // the second half adds its dQ and dK to the first's.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "psa_device.hpp"
@@ -578,10 +579,13 @@ struct PsaBwdF32Args {
   float* dqkv;         // [BH * 4KD, N]
   int BH, N, KD, j;    // j: the V half (0: lo, 1: hi)
   float scale;
+  int bh0;             // first batch-head of this launch
 };
 
-constexpr int kF32Threads = 128;   // one row per thread
-constexpr int kF32Rows = 32;       // rows per LDS tile
+constexpr int kF32Threads = 128;
+constexpr int kF32Rows = 32;                        // rows per LDS tile
+constexpr int kF32Lanes = 4;                        // lanes per output pixel
+constexpr int kF32Out = kF32Threads / kF32Lanes;    // output pixels per workgroup
 
 // Thread element i of a [kF32Rows][cols] LDS tile filled from channel rows:
 // pixels (tile rows) fastest, as they are contiguous in NCHW.
@@ -589,6 +593,16 @@ __device__ __forceinline__ void f32_rc(int i, int& r, int& d) {
   const int e = static_cast<int>(threadIdx.x) + i * kF32Threads;
   r = e % kF32Rows;
   d = e / kF32Rows;
+}
+
+// Adds the partial sums x[0..D) of the four lanes of an output pixel (lanes
+// 4i..4i+3); every lane ends with the total.
+template <int D>
+__device__ __forceinline__ void sum_lanes(float (&x)[D]) {
+#pragma unroll
+  for (int m = 1; m < kF32Lanes; m <<= 1)
+#pragma unroll
+    for (int d = 0; d < D; ++d) x[d] += __shfl_xor(x[d], m);
 }
 
 // -Delta_j = -sum over half j's channels of dO * O, one thread per pixel.
@@ -604,16 +618,19 @@ __global__ __launch_bounds__(256) void psa_bwd_delta_f32(PsaBwdF32Args a) {
   a.delta[i] = -s;
 }
 
-// dK (summed over the halves) and dV_j: one thread per key, queries staged through LDS.
+// dK (summed over the halves) and dV_j: four lanes per key, lane l taking queries
+// l, l+4, ... of each tile staged through LDS; the lanes' partial sums are added
+// at the end.
 template <int KD>
 __global__ __launch_bounds__(kF32Threads) void psa_bwd_dkdv_f32(PsaBwdF32Args a) {
   __shared__ float qs[kF32Rows][KD];
   __shared__ float gs[kF32Rows][KD];
   __shared__ float ls[kF32Rows], dls[kF32Rows];
   const int N = a.N;
-  const int blocks = (N + kF32Threads - 1) / kF32Threads;
-  const int bh = blockIdx.x / blocks;
-  const int m = (blockIdx.x % blocks) * kF32Threads + threadIdx.x;
+  const int blocks = (N + kF32Out - 1) / kF32Out;
+  const int bh = a.bh0 + static_cast<int>(blockIdx.x / blocks);
+  const int lane = threadIdx.x % kF32Lanes;
+  const int m = (blockIdx.x % blocks) * kF32Out + threadIdx.x / kF32Lanes;
   const bool ok = m < N;
   const int mc = ok ? m : 0;
   const float* Q = a.qkv + static_cast<int64_t>(bh) * 4 * KD * N;   // channel rows of this head
@@ -641,7 +658,7 @@ __global__ __launch_bounds__(kF32Threads) void psa_bwd_dkdv_f32(PsaBwdF32Args a)
     }
     __syncthreads();
     const int cnt = min(kF32Rows, N - q0);
-    for (int r = 0; r < cnt; ++r) {
+    for (int r = lane; r < cnt; r += kF32Lanes) {
       const float sc = dot_f32<KD>(qs[r], kr);
       const float dp = dot_f32<KD>(gs[r], vr);
       const float p = expf(sc * a.scale - ls[r]);
@@ -653,36 +670,44 @@ __global__ __launch_bounds__(kF32Threads) void psa_bwd_dkdv_f32(PsaBwdF32Args a)
       }
     }
   }
+  sum_lanes<KD>(dk);
+  sum_lanes<KD>(dv);
   if (!ok) return;
+  // This lane stores the channels d = lane (mod 4).
+  auto mine = [&](int d) { return d % kF32Lanes == lane; };
   float* out = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N;
   const float* res = a.dvres ? a.dvres + (static_cast<int64_t>(bh) * 2 + a.j) * KD * N : nullptr;
   float* pk = out + static_cast<int64_t>(KD) * N + m;             // dK channel rows
   float* pv = out + static_cast<int64_t>(2 + a.j) * KD * N + m;   // dV_j channel rows
   if (a.j == 0) {
 #pragma unroll
-    for (int d = 0; d < KD; ++d) pk[static_cast<int64_t>(d) * N] = dk[d] * a.scale;
+    for (int d = 0; d < KD; ++d)
+      if (mine(d)) pk[static_cast<int64_t>(d) * N] = dk[d] * a.scale;
   } else {
-    move_batched<KD>([&](int d) { return pk[static_cast<int64_t>(d) * N]; },
-                     [&](int d, float x) { pk[static_cast<int64_t>(d) * N] = x + dk[d] * a.scale; });
+    move_batched<KD>([&](int d) { return mine(d) ? pk[static_cast<int64_t>(d) * N] : 0.0f; },
+                     [&](int d, float x) { if (mine(d)) pk[static_cast<int64_t>(d) * N] = x + dk[d] * a.scale; });
   }
   if (res) {
-    move_batched<KD>([&](int d) { return res[static_cast<int64_t>(d) * N + m]; },
-                     [&](int d, float x) { pv[static_cast<int64_t>(d) * N] = dv[d] + x; });
+    move_batched<KD>([&](int d) { return mine(d) ? res[static_cast<int64_t>(d) * N + m] : 0.0f; },
+                     [&](int d, float x) { if (mine(d)) pv[static_cast<int64_t>(d) * N] = dv[d] + x; });
   } else {
 #pragma unroll
-    for (int d = 0; d < KD; ++d) pv[static_cast<int64_t>(d) * N] = dv[d];
+    for (int d = 0; d < KD; ++d)
+      if (mine(d)) pv[static_cast<int64_t>(d) * N] = dv[d];
   }
 }
 
-// dQ (summed over the halves): one thread per query, keys staged through LDS.
+// dQ (summed over the halves): four lanes per query, lane l taking keys l, l+4,
+// ... of each tile staged through LDS; the lanes' partial sums are added at the end.
 template <int KD>
 __global__ __launch_bounds__(kF32Threads) void psa_bwd_dq_f32(PsaBwdF32Args a) {
   __shared__ float ks[kF32Rows][KD];
   __shared__ float vs[kF32Rows][KD];
   const int N = a.N;
-  const int blocks = (N + kF32Threads - 1) / kF32Threads;
-  const int bh = blockIdx.x / blocks;
-  const int n = (blockIdx.x % blocks) * kF32Threads + threadIdx.x;
+  const int blocks = (N + kF32Out - 1) / kF32Out;
+  const int bh = a.bh0 + static_cast<int>(blockIdx.x / blocks);
+  const int lane = threadIdx.x % kF32Lanes;
+  const int n = (blockIdx.x % blocks) * kF32Out + threadIdx.x / kF32Lanes;
   const bool ok = n < N;
   const int nc = ok ? n : 0;
   const float* Q = a.qkv + static_cast<int64_t>(bh) * 4 * KD * N;
@@ -710,7 +735,7 @@ __global__ __launch_bounds__(kF32Threads) void psa_bwd_dq_f32(PsaBwdF32Args a) {
         [&](int i, float x) { int r, d; f32_rc(i, r, d); vs[r][d] = x; });
     __syncthreads();
     const int cnt = min(kF32Rows, N - m0);
-    for (int r = 0; r < cnt; ++r) {
+    for (int r = lane; r < cnt; r += kF32Lanes) {
       const float sc = dot_f32<KD>(qr, ks[r]);
       const float dp = dot_f32<KD>(gr, vs[r]);
       const float ds = expf(sc * a.scale - lse) * (dp + dl);
@@ -718,14 +743,17 @@ __global__ __launch_bounds__(kF32Threads) void psa_bwd_dq_f32(PsaBwdF32Args a) {
       for (int d = 0; d < KD; ++d) dq[d] = fmaf(ds, ks[r][d], dq[d]);
     }
   }
+  sum_lanes<KD>(dq);
   if (!ok) return;
+  auto mine = [&](int d) { return d % kF32Lanes == lane; };   // this lane's channels
   float* p = a.dqkv + static_cast<int64_t>(bh) * 4 * KD * N + n;   // dQ channel rows
   if (a.j == 0) {
 #pragma unroll
-    for (int d = 0; d < KD; ++d) p[static_cast<int64_t>(d) * N] = dq[d] * a.scale;
+    for (int d = 0; d < KD; ++d)
+      if (mine(d)) p[static_cast<int64_t>(d) * N] = dq[d] * a.scale;
   } else {
-    move_batched<KD>([&](int d) { return p[static_cast<int64_t>(d) * N]; },
-                     [&](int d, float x) { p[static_cast<int64_t>(d) * N] = x + dq[d] * a.scale; });
+    move_batched<KD>([&](int d) { return mine(d) ? p[static_cast<int64_t>(d) * N] : 0.0f; },
+                     [&](int d, float x) { if (mine(d)) p[static_cast<int64_t>(d) * N] = x + dq[d] * a.scale; });
   }
 }
 
@@ -733,14 +761,23 @@ template <int KD>
 hipError_t run_psa_bwd_f32(PsaBwdF32Args a, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.BH) * a.N;
   const dim3 grid_delta(static_cast<unsigned>((rows + 255) / 256));
-  const dim3 grid(static_cast<unsigned>(a.BH) * ((a.N + kF32Threads - 1) / kF32Threads));
+  // Batch-heads per launch, so that a launch holds at most 2^31 work-items.
+  const int64_t per_bh = (a.N + kF32Out - 1) / kF32Out;
+  const int64_t max_bh = std::max<int64_t>(1, (int64_t(1) << 31) / (per_bh * kF32Threads));
   for (int j = 0; j < 2; ++j) {   // the second half adds its dQ and dK to the first's
     a.j = j;
     psa_bwd_delta_f32<<<grid_delta, 256, 0, stream>>>(a);
-    psa_bwd_dkdv_f32<KD><<<grid, kF32Threads, 0, stream>>>(a);
-    psa_bwd_dq_f32<KD><<<grid, kF32Threads, 0, stream>>>(a);
-    const hipError_t err = hipGetLastError();
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    for (int64_t b0 = 0; b0 < a.BH; b0 += max_bh) {
+      PsaBwdF32Args c = a;
+      c.bh0 = static_cast<int>(b0);
+      const dim3 grid(static_cast<unsigned>(per_bh * std::min<int64_t>(max_bh, a.BH - b0)));
+      psa_bwd_dkdv_f32<KD><<<grid, kF32Threads, 0, stream>>>(c);
+      psa_bwd_dq_f32<KD><<<grid, kF32Threads, 0, stream>>>(c);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
   }
   return hipSuccess;
 }

@@ -99,10 +99,14 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // hipGetLastError(); the launchers report their launches with that call. It is
 // cleared first, so that a failure left behind by an unrelated earlier call is
 // not reported as this entry point's launch failure. (An error that poisons the
-// device stays sticky and is still reported.)
+// device stays sticky and is still reported.) Before the launches it runs the
+// device set-up, which does its work on the first call on each device only.
 template <typename Launch>
 psa_status launched(const char* fn, Launch&& launch) {
   (void)hipGetLastError();
+  const hipError_t init = psa::init_device();
+  if (init != hipSuccess)
+    return fail(PSA_ERR_LAUNCH, fn, "device set-up failed: %s", hipGetErrorString(init));
   const hipError_t e = launch();
   if (e != hipSuccess) return fail(PSA_ERR_LAUNCH, fn, "launch failed: %s", hipGetErrorString(e));
   return ok();

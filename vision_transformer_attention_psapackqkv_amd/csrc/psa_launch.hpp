@@ -47,6 +47,14 @@ hipError_t launch_fa2_bwd(const void* q, const void* k, const void* v, const voi
 // fa2_bwd with -Delta in the library's own device scratch (no allocation, no
 // workspace argument): at most kNoAllocScratchBytes / 8 rows (BH * n_q).
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+
+// Set-up of the current device, which every entry point runs before its
+// launches: the first call on a device looks up the device address of
+// fa2_bwd_noalloc's scratch array (later calls return at once). Calls that
+// arrive while it runs wait for it, so that the lookup never overlaps a
+// launch of this library's kernels on another thread (HIP's symbol lookup
+// has aborted the process when it did).
+hipError_t init_device();
 hipError_t launch_fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
                                   int BH, int n_q, int n_k, int D, float scale, bool bf16,
