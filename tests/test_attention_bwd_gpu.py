@@ -110,3 +110,29 @@ def test_fa2_bwd_zero_queries(D):
     assert_attention_close(to_f64(dv), want_dv, "bf16", "dV vs (1/n_k) sum dO")
     assert float(dk.float().abs().max()) == 0.0, "dK is not zero"
     _check((dq, dk, dv), q, k, v, do, "bf16")
+
+
+def test_fa2_f32_more_batch_heads_than_one_launch():
+    """float32 fa2_fwd and fa2_bwd with 2^22 + 3 batch-heads of 128 queries: four lanes per
+    query make 2^31 + 1,536 work-items in the forward and dQ kernels, so each is split into two
+    launches by batch-head (the second covers the last three). Inputs are drawn on the GPU (~150 GB
+    in all); the first, a middle and the last three batch-heads are checked against the oracle."""
+    dev = device()
+    BH, nq, nk, D = (1 << 22) + 3, 128, 5, 16
+    announce(f"fa2 f32 BH={BH} q{nq} k{nk} d{D}: two launches per kernel")
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    q, k, v, do = (torch.rand(shape, generator=g, device=dev).mul_(2).sub_(1)
+                   for shape in ((BH, nq, D), (BH, nk, D), (BH, nk, D), (BH, nq, D)))
+    s = D ** -0.5
+    o, lse = psa.fa2_fwd(q, k, v, scale=s)
+    dq, dk, dv = psa.fa2_bwd(q, k, v, o, do, lse, scale=s)
+    torch.cuda.synchronize()
+    sel = torch.tensor([0, BH // 2, BH - 3, BH - 2, BH - 1], device=dev)
+    pick = lambda t: to_f64(t.index_select(0, sel))
+    want_o, want_lse = O.attention(pick(q), pick(k), pick(v), s)
+    assert_attention_close(pick(o), want_o, "f32", "fa2_fwd O, sampled batch-heads")
+    assert np.abs(pick(lse) - want_lse).max() < 1e-4
+    want = O.attention_bwd(pick(q), pick(k), pick(v), pick(do), s)
+    for name, got, w in zip(("dQ", "dK", "dV"), (dq, dk, dv), want):
+        assert_attention_close(pick(got), w, "f32", f"fa2_bwd {name}, sampled batch-heads")
