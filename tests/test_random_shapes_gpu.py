@@ -3,7 +3,8 @@ and backward, each against the float64 oracle.
 
 The shapes are drawn once from a fixed seed (so the list is the same on every run), over
 every key/head dim, maps and sequence lengths that are and are not multiples of the tile
-sizes and of 8 (the directly staged and the register-staged kernels), and n_q != n_k.
+sizes and of 8 (the directly staged and the register-staged kernels), and n_q != n_k; the PSA
+maps in bf16 and, from a second draw, in float32.
 """
 import numpy as np
 import pytest
@@ -48,30 +49,37 @@ def _psa_id(s):
     return "B{}h{}kd{}_{}x{}".format(*s)
 
 
-@pytest.mark.parametrize("shape", PSA_RANDOM, ids=_psa_id)
-def test_random_psa_fwd_bwd(shape):
+# float32 maps (the VALU kernels, four lanes per row) drawn the same way from another seed
+PSA_RANDOM_F32 = _psa_shapes(6, 2028)
+PSA_CASES = [(s, "bf16") for s in PSA_RANDOM] + [(s, "f32") for s in PSA_RANDOM_F32]
+
+
+@pytest.mark.parametrize("case", PSA_CASES, ids=lambda c: _psa_id(c[0]) + "_" + c[1])
+def test_random_psa_fwd_bwd(case):
     dev = device()
+    shape, dt = case
     B, h, KD, H, W = shape
-    announce(f"random psa fwd/bwd {_psa_id(shape)}")
+    announce(f"random psa fwd/bwd {_psa_id(shape)} {dt}")
     seed = 7000 + B * 1000 + h * 100 + KD + H * W
-    qkv = I.make_qkv(B, h, KD, H, W, seed=seed)
+    qkv = I.make_qkv(B, h, KD, H, W, dtype=dt, seed=seed)
     x = qkv.to(dev)
     out, vres, lse = psa.psa_attention_fwd(x, h, KD)
     want_out, _, want_lse = O.psa_forward(to_f64(qkv), B, h, KD, H, W)
-    assert_attention_close(to_f64(out), want_out, "bf16", "random psa_attention_fwd out")
-    assert_lse_close(to_f64(lse), want_lse, "bf16", "random psa_attention_fwd")
+    assert_attention_close(to_f64(out), want_out, dt, "random psa_attention_fwd out")
+    assert_lse_close(to_f64(lse), want_lse, dt, "random psa_attention_fwd")
     want_v = O.extract_v(O.pack_qkv(bits(qkv), B, h, KD, H, W), B, h, KD, H, W)
     assert np.array_equal(bits(vres), want_v), "V residual differs"
 
     rng = np.random.default_rng(seed + 1)
-    dout = torch.from_numpy(rng.standard_normal(tuple(out.shape)).astype(np.float32)).to(torch.bfloat16)
-    dv = torch.from_numpy(rng.standard_normal(tuple(out.shape)).astype(np.float32)).to(torch.bfloat16)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    dout = torch.from_numpy(rng.standard_normal(tuple(out.shape)).astype(np.float32)).to(tdt)
+    dv = torch.from_numpy(rng.standard_normal(tuple(out.shape)).astype(np.float32)).to(tdt)
     got = to_f64(psa.psa_attention_bwd(x, out, lse, dout.to(dev), h, KD, dv=dv.to(dev)))
     want = O.psa_backward(to_f64(qkv), to_f64(dout), to_f64(dv), B, h, KD, H, W)
     g = got.reshape(B, h, 4, KD, H * W)
     wr = want.reshape(B, h, 4, KD, H * W)
     for s, name in enumerate(("dQ", "dK", "dV_lo", "dV_hi")):
-        assert_attention_close(g[:, :, s], wr[:, :, s], "bf16", f"random psa_attention_bwd {name}")
+        assert_attention_close(g[:, :, s], wr[:, :, s], dt, f"random psa_attention_bwd {name}")
 
 
 @pytest.mark.parametrize("shape", FA2_RANDOM, ids=lambda s: "BH{}_q{}_k{}_d{}_{}".format(*s))
