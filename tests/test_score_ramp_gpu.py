@@ -116,3 +116,48 @@ def test_ramp_psa_bwd(shape):
     wr = want.reshape(B, h, 4, KD, H * W)
     for s, name in enumerate(("dQ", "dK", "dV_lo", "dV_hi")):
         assert_attention_close(g[:, :, s], wr[:, :, s], "bf16", f"ramp psa_attention_bwd {name}")
+
+
+# float32: the VALU kernels, whose four lanes per row each keep their own running maximum and
+# are combined at the end (rising rows: lanes whose maxima differ by the key stride's 12 log2
+# units per 64 keys). The bf16-stored ramp values are exact in float32.
+@pytest.mark.parametrize("shape", [(1, 1, 16, 8, 8), (2, 2, 32, 24, 24), (1, 1, 128, 16, 16), (1, 2, 64, 9, 7)],
+                         ids=_psa_id)
+def test_ramp_psa_fwd_bwd_f32(shape):
+    dev = device()
+    B, h, KD, H, W = shape
+    announce(f"ramp psa_attention_fwd/bwd f32 {_psa_id(shape)}")
+    qkv = I.make_ramp_qkv(B, h, KD, H, W, score_step=_step(KD), seed=700 + KD + H * W).float()
+    x = qkv.to(dev)
+    out, vres, lse = psa.psa_attention_fwd(x, h, KD)
+    want_out, _, want_lse = O.psa_forward(to_f64(qkv), B, h, KD, H, W)
+    assert_attention_close(to_f64(out), want_out, "f32", "ramp f32 psa_attention_fwd out")
+    assert_lse_close(to_f64(lse), want_lse, "f32", "ramp f32 psa_attention_fwd")
+    rng = np.random.default_rng(701 + KD)
+    dout = torch.from_numpy(0.25 * rng.standard_normal(tuple(out.shape)).astype(np.float32))
+    got = to_f64(psa.psa_attention_bwd(x, out, lse, dout.to(dev), h, KD))
+    want = O.psa_backward(to_f64(qkv), to_f64(dout), None, B, h, KD, H, W)
+    g = got.reshape(B, h, 4, KD, H * W)
+    wr = want.reshape(B, h, 4, KD, H * W)
+    for s, name in enumerate(("dQ", "dK", "dV_lo", "dV_hi")):
+        assert_attention_close(g[:, :, s], wr[:, :, s], "f32", f"ramp f32 psa_attention_bwd {name}")
+
+
+@pytest.mark.parametrize("shape", [(2, 300, 260, 32), (1, 100, 1500, 64), (1, 70, 90, 128)],
+                         ids=lambda s: "BH{}_q{}_k{}_d{}".format(*s))
+def test_ramp_fa2_fwd_bwd_f32(shape):
+    dev = device()
+    BH, nq, nk, D = shape
+    announce(f"ramp fa2_fwd/fa2_bwd f32 BH{BH} q{nq} k{nk} d{D}")
+    q, k, v, do = (t.float() for t in I.make_ramp_attention_inputs(BH, nq, nk, D, score_step=_step(D),
+                                                                   seed=800 + nq + D, with_dout=True))
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = psa.fa2_fwd(qd, kd, vd)
+    s = D ** -0.5
+    want_o, want_lse = O.attention(to_f64(q), to_f64(k), to_f64(v), s)
+    assert_attention_close(to_f64(o), want_o, "f32", "ramp f32 fa2_fwd O")
+    assert_lse_close(to_f64(lse), want_lse, "f32", "ramp f32 fa2_fwd")
+    grads = psa.fa2_bwd(qd, kd, vd, o, dod, lse)
+    want = O.attention_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), s)
+    for name, got, w in zip(("dQ", "dK", "dV"), grads, want):
+        assert_attention_close(to_f64(got), w, "f32", f"ramp f32 fa2_bwd {name}")
