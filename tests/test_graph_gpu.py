@@ -152,3 +152,18 @@ def test_fa2_and_layout_in_a_graph():
         launches()
     y = torch.randn(1 << 20, device=dev)
     _replays_match(g, [packed, o2, lse, merged, vres] + grads, eager, lambda: y.mul_(1.5))
+
+
+def test_first_library_calls_under_capture():
+    """In a fresh process, the library's first calls (which run its per-device set-up) are made
+    under graph capture; the replays equal the eager calls (`graph_first_child.py`)."""
+    import os
+    import subprocess
+    import sys
+    device()
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "graph_first_child.py")
+    announce("first library calls of a process under graph capture (child process)")
+    r = subprocess.run([sys.executable, "-u", child], capture_output=True, text=True, timeout=240)
+    print(r.stdout[-3000:], r.stderr[-3000:], flush=True)
+    assert r.returncode == 0, f"child exited {r.returncode}"
+    assert "ALL OK" in r.stdout
